@@ -1,0 +1,142 @@
+"""fp64 CPU oracle for exact attention (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or calls it, and this package imports
+nothing from the product: the two sides share only the seeded input
+generators, which hold none of the method's arithmetic.
+
+``attn_oracle.c`` computes the plain definition of attention (scores, masked
+softmax, weighted sum of values, log-sum-exp) in double precision; see the
+header of that file for the passages it follows.  ``online.py`` holds the
+pages' tiled online-softmax algorithm and the split-KV merge, in fp64, as a
+second test reference.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "attn_oracle.c")
+_LIB = os.path.join(_HERE, "libattn_oracle.so")
+
+F32, BF16, F64 = 0, 1, 2
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP) next to its source."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", _SRC, "-o", tmp, "-lm"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def load_library(path: str):
+    """Open a compiled oracle library and declare its C signatures."""
+    lib = ctypes.CDLL(path)
+    vp, dp, lp, ip = ctypes.c_void_p, ctypes.c_double, ctypes.c_long, ctypes.c_int
+    lib.oracle_attention.argtypes = [vp, vp, vp, ip, vp, vp, lp, lp, lp, lp, lp, lp, dp, ip]
+    lib.oracle_attention.restype = ip
+    lib.oracle_attention_rows.argtypes = [vp, vp, vp, ip, vp, lp, vp, vp,
+                                          lp, lp, lp, lp, lp, lp, dp, ip]
+    lib.oracle_attention_rows.restype = ip
+    lib.oracle_decode.argtypes = [vp, vp, vp, ip, vp, vp, vp, lp, lp, lp, lp, lp, dp]
+    lib.oracle_decode.restype = ip
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = ip
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build()
+        _lib = load_library(_LIB)
+    return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().oracle_num_threads())
+
+
+def _dtype_code(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:       # bf16 bit patterns
+        return BF16
+    if a.dtype == np.float64:
+        return F64
+    raise TypeError(f"oracle inputs must be float32, float64 or bf16 bits (uint16), got {a.dtype}")
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _prep(*arrays):
+    arrays = [np.ascontiguousarray(a) for a in arrays]
+    codes = {_dtype_code(a) for a in arrays}
+    if len(codes) != 1:
+        raise TypeError("q, k and v must share one storage dtype")
+    return arrays, codes.pop()
+
+
+def attention(q, k, v, scale: float, causal: bool):
+    """O [B,H,N_q,d] and LSE [B,H,N_q] in fp64 for q [B,H,N_q,d], k/v [B,H_kv,N_k,d]."""
+    (q, k, v), code = _prep(q, k, v)
+    B, H, N_q, d = q.shape
+    Bk, H_kv, N_k, dk = k.shape
+    if Bk != B or dk != d or v.shape != k.shape:
+        raise ValueError("shape mismatch between q, k and v")
+    o = np.empty((B, H, N_q, d), np.float64)
+    lse = np.empty((B, H, N_q), np.float64)
+    rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), code, _ptr(o), _ptr(lse),
+                                  B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)))
+    if rc != 0:
+        raise ValueError(f"oracle_attention failed with code {rc}")
+    return o, lse
+
+
+def attention_rows(q, k, v, rows, scale: float, causal: bool):
+    """O and LSE for the (b, h, i) query rows listed in ``rows`` only."""
+    (q, k, v), code = _prep(q, k, v)
+    B, H, N_q, d = q.shape
+    _, H_kv, N_k, _ = k.shape
+    rows = np.ascontiguousarray(np.asarray(rows, dtype=np.int64).reshape(-1, 3))
+    n = rows.shape[0]
+    o = np.empty((n, d), np.float64)
+    lse = np.empty((n,), np.float64)
+    rc = _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), code, _ptr(rows), n,
+                                       _ptr(o), _ptr(lse), B, H, H_kv, N_q, N_k, d,
+                                       float(scale), int(bool(causal)))
+    if rc != 0:
+        raise ValueError(f"oracle_attention_rows failed with code {rc}")
+    return o, lse
+
+
+def decode(q, k_cache, v_cache, seq_lens, scale: float):
+    """One decode step: O [B,H,d] and LSE [B,H] in fp64."""
+    (q, k_cache, v_cache), code = _prep(q, k_cache, v_cache)
+    B, H, d = q.shape
+    _, H_kv, N_max, _ = k_cache.shape
+    lens = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    if lens.shape != (B,):
+        raise ValueError("seq_lens must have one entry per sequence")
+    o = np.empty((B, H, d), np.float64)
+    lse = np.empty((B, H), np.float64)
+    rc = _load().oracle_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), code, _ptr(lens),
+                               _ptr(o), _ptr(lse), B, H, H_kv, N_max, d, float(scale))
+    if rc != 0:
+        raise ValueError(f"oracle_decode failed with code {rc}")
+    return o, lse

@@ -1,0 +1,374 @@
+"""Pins of the fp64 oracle to facts other than itself.
+
+Each test ties the oracle to a closed form, a special case, an independent
+library routine, an invariant of the definition, or brute force on tiny
+inputs, so that a plausible slip in it (a dropped scale, a wrong mask edge, a
+transposed head map, an lse without its max) fails at least one of them.
+tests/test_oracle_mutants.py plants such slips in a copy of the oracle and
+checks that this suite catches every one.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import online
+from transformer_attention_fa_amd import inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+TOL = 1e-12
+
+
+def rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def visible_count(i, n_q, n_k, causal):
+    if not causal:
+        return n_k
+    return max(0, min(n_k, i + (n_k - n_q) + 1))
+
+
+# --------------------------------------------------------------------------
+# P-a: softmax rows sum to one; masked probabilities are exactly zero.
+# With V = identity (d = N_k) the output row is the probability row itself.
+# ("Attention variants" §3: P = softmax(S); "Attention mechanism evolution",
+#  MHA code: masked scores filled with -inf before the softmax.)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_q,n_k", [(7, 7), (5, 9), (9, 5)])
+def test_probability_rows_sum_to_one(causal, n_q, n_k):
+    q = rand((1, 2, n_q, n_k), 1)
+    k = rand((1, 2, n_k, n_k), 2)
+    v = np.broadcast_to(np.eye(n_k), (1, 2, n_k, n_k)).copy()
+    p, lse = oracle.attention(q, k, v, 0.7, causal)
+    for h in range(2):
+        for i in range(n_q):
+            nv = visible_count(i, n_q, n_k, causal)
+            row = p[0, h, i]
+            assert np.all(row >= 0)
+            assert np.all(row[nv:] == 0.0)
+            if nv:
+                assert abs(row.sum() - 1.0) <= TOL
+            else:
+                assert np.all(row == 0.0) and np.isneginf(lse[0, h, i])
+
+
+# --------------------------------------------------------------------------
+# P-b: Q = 0 gives equal weights, so each output row is the mean of the
+# visible V rows and lse = ln(number of visible keys).
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_q,n_k", [(6, 6), (4, 10), (10, 4)])
+def test_zero_query_closed_form(causal, n_q, n_k):
+    d = 5
+    q = np.zeros((2, 3, n_q, d))
+    k = rand((2, 3, n_k, d), 3)
+    v = rand((2, 3, n_k, d), 4)
+    o, lse = oracle.attention(q, k, v, 0.3, causal)
+    for b in range(2):
+        for h in range(3):
+            for i in range(n_q):
+                nv = visible_count(i, n_q, n_k, causal)
+                if nv == 0:
+                    assert np.all(o[b, h, i] == 0) and np.isneginf(lse[b, h, i])
+                    continue
+                np.testing.assert_allclose(o[b, h, i], v[b, h, :nv].mean(axis=0), atol=TOL, rtol=0)
+                assert abs(lse[b, h, i] - math.log(nv)) <= TOL
+
+
+# --------------------------------------------------------------------------
+# P-c: head sharing.  GQA equals MHA on K/V repeated over rep = H/H_kv
+# consecutive query heads ("Attention variants" §2 repeat_interleave;
+# "Attention mechanism evolution" _repeat_kv); H_kv = 1 is MQA; the map is
+# g = h // rep, not h % H_kv.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("h,h_kv", [(8, 2), (6, 3), (4, 1), (4, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_gqa_equals_repeated_mha(h, h_kv, causal):
+    q = rand((2, h, 6, 4), 5)
+    k = rand((2, h_kv, 6, 4), 6)
+    v = rand((2, h_kv, 6, 4), 7)
+    rep = h // h_kv
+    o, lse = oracle.attention(q, k, v, 0.5, causal)
+    o2, lse2 = oracle.attention(q, np.repeat(k, rep, axis=1), np.repeat(v, rep, axis=1), 0.5, causal)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(lse, lse2)
+    # and per head against a one-head call on the KV head it must read
+    for hh in range(h):
+        o1, l1 = oracle.attention(q[:, hh:hh + 1], k[:, hh // rep:hh // rep + 1], v[:, hh // rep:hh // rep + 1],
+                                  0.5, causal)
+        np.testing.assert_array_equal(o[:, hh:hh + 1], o1)
+        np.testing.assert_array_equal(lse[:, hh:hh + 1], l1)
+
+
+def test_shape_rules_enforced():
+    q = rand((1, 6, 3, 4), 1)
+    k = rand((1, 4, 3, 4), 2)
+    with pytest.raises(ValueError):          # H must be a multiple of H_kv
+        oracle.attention(q, k, k, 1.0, False)
+
+
+# --------------------------------------------------------------------------
+# P-d: the pages' tiled online softmax reaches the two-pass result for every
+# block size ("Attention variants" §3 and §5.5), on tiny inputs.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n_q,n_k", [(16, 16), (11, 16), (16, 11), (1, 9)])
+def test_tiled_online_softmax_equals_two_pass(causal, n_q, n_k):
+    d = 8
+    q = rand((1, 1, n_q, d), 11)
+    k = rand((1, 1, n_k, d), 12) * 3.0       # sharp rows: the max moves often
+    v = rand((1, 1, n_k, d), 13)
+    o, lse = oracle.attention(q, k, v, 0.6, causal)
+    for bq in (1, 2, 3, 7, 64, n_q):
+        for bk in (1, 2, 3, 7, 64, n_k):
+            ot, lt = online.tiled_head(q[0, 0], k[0, 0], v[0, 0], 0.6, causal, bq, bk)
+            np.testing.assert_allclose(ot, o[0, 0], atol=TOL, rtol=0)
+            fin = np.isfinite(lse[0, 0])
+            np.testing.assert_allclose(lt[fin], lse[0, 0][fin], atol=TOL, rtol=0)
+            assert np.array_equal(np.isneginf(lt), np.isneginf(lse[0, 0]))
+
+
+# --------------------------------------------------------------------------
+# P-e: edges of the causal mask.  Row 0 of a square causal problem sees only
+# key 0: o_0 = v_0 and lse_0 = s_00.  With one key every row returns v_0.
+# --------------------------------------------------------------------------
+def test_causal_row_zero_and_single_key():
+    d, n = 6, 7
+    q = rand((1, 1, n, d), 21)
+    k = rand((1, 1, n, d), 22)
+    v = rand((1, 1, n, d), 23)
+    scale = 0.37
+    o, lse = oracle.attention(q, k, v, scale, True)
+    np.testing.assert_array_equal(o[0, 0, 0], v[0, 0, 0])
+    s00 = scale * sum(float(a) * float(b) for a, b in zip(q[0, 0, 0], k[0, 0, 0]))
+    assert abs(lse[0, 0, 0] - s00) <= TOL
+    o1, l1 = oracle.attention(q, k[:, :, :1], v[:, :, :1], scale, False)
+    for i in range(n):
+        np.testing.assert_allclose(o1[0, 0, i], v[0, 0, 0], atol=TOL, rtol=0)
+        s = scale * float(np.dot(q[0, 0, i], k[0, 0, 0]))
+        assert abs(l1[0, 0, i] - s) <= TOL
+
+
+def test_one_dominant_key_at_extreme_scale():
+    """Scores spread by thousands: every weight but the largest underflows to 0,
+    so o = v of the top key and lse = its score; a softmax that does not subtract
+    the row maximum overflows instead."""
+    n, d = 6, 3
+    q = np.zeros((1, 1, 2, d))
+    q[0, 0, :, 0] = 1.0
+    k = np.zeros((1, 1, n, d))
+    k[0, 0, :, 0] = [-2000.0, 500.0, 3000.0, -100.0, 1500.0, 0.0]   # key 2 dominates, key 0 is lowest
+    v = rand((1, 1, n, d), 25)
+    for causal in (False,):
+        o, lse = oracle.attention(q, k, v, 1.0, causal)
+        np.testing.assert_array_equal(o[0, 0, 0], v[0, 0, 2])
+        assert lse[0, 0, 0] == 3000.0
+
+
+def test_rows_with_no_visible_key():
+    """Causal with N_q > N_k: the first N_q - N_k rows see nothing (o = 0, lse = -inf)."""
+    q = rand((1, 1, 6, 3), 31)
+    k = rand((1, 1, 2, 3), 32)
+    o, lse = oracle.attention(q, k, k, 1.0, True)
+    assert np.all(o[0, 0, :4] == 0) and np.all(np.isneginf(lse[0, 0, :4]))
+    assert np.all(np.isfinite(lse[0, 0, 4:]))
+
+
+# --------------------------------------------------------------------------
+# P-f: invariants of the definition.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+def test_linear_in_v_and_shift_invariant(causal):
+    b, h, n, d = 2, 2, 9, 5
+    q, k, v = rand((b, h, n, d), 41), rand((b, h, n, d), 42), rand((b, h, n, d), 43)
+    o, lse = oracle.attention(q, k, v, 0.8, causal)
+    c = rand((d,), 44)
+    o2, lse2 = oracle.attention(q, k, 2.5 * v + c, 0.8, causal)
+    np.testing.assert_allclose(o2, 2.5 * o + c, atol=1e-11, rtol=0)
+    np.testing.assert_array_equal(lse2, lse)
+    # adding one vector u to every key shifts row i's scores by scale*<q_i,u>:
+    # o is unchanged, lse moves by exactly that amount
+    u = rand((d,), 45)
+    o3, lse3 = oracle.attention(q, k + u, v, 0.8, causal)
+    np.testing.assert_allclose(o3, o, atol=1e-11, rtol=0)
+    np.testing.assert_allclose(lse3, lse + 0.8 * (q @ u), atol=1e-11, rtol=0)
+
+
+def test_joint_key_value_permutation():
+    q, k, v = rand((1, 2, 5, 4), 51), rand((1, 2, 8, 4), 52), rand((1, 2, 8, 4), 53)
+    perm = np.random.default_rng(54).permutation(8)
+    o, lse = oracle.attention(q, k, v, 0.9, False)
+    o2, lse2 = oracle.attention(q, k[:, :, perm], v[:, :, perm], 0.9, False)
+    np.testing.assert_allclose(o2, o, atol=TOL, rtol=0)
+    np.testing.assert_allclose(lse2, lse, atol=TOL, rtol=0)
+
+
+def test_scale_is_applied_to_scores():
+    """scale*QK^T: doubling the scale equals doubling Q."""
+    q, k, v = rand((1, 1, 6, 4), 61), rand((1, 1, 6, 4), 62), rand((1, 1, 6, 4), 63)
+    o, lse = oracle.attention(q, k, v, 0.8, True)
+    o2, lse2 = oracle.attention(q * 2.0, k, v, 0.4, True)
+    np.testing.assert_allclose(o2, o, atol=TOL, rtol=0)
+    np.testing.assert_allclose(lse2, lse, atol=TOL, rtol=0)
+    o3, _ = oracle.attention(q, k, v, 0.0, False)          # scale 0: plain mean of V
+    np.testing.assert_allclose(o3[0, 0], np.broadcast_to(v[0, 0].mean(0), (6, 4)), atol=TOL, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# P-g: independent library routine.  The pages' own PyTorch form
+# (softmax(q k^T * scale, masked with -inf) @ v, K/V repeated over the group)
+# run by torch on the CPU in fp64, and torch's own scaled_dot_product_attention.
+# --------------------------------------------------------------------------
+def _torch_reference(q, k, v, scale, causal):
+    import torch
+    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)).double() for x in (q, k, v))
+    rep = qt.shape[1] // kt.shape[1]
+    kt = kt.repeat_interleave(rep, dim=1)
+    vt = vt.repeat_interleave(rep, dim=1)
+    s = torch.matmul(qt, kt.transpose(-2, -1).contiguous()) * scale
+    n_q, n_k = s.shape[-2:]
+    if causal:
+        keep = torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=n_k - n_q)
+        s = s.masked_fill(~keep, float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    o = torch.matmul(torch.softmax(s, dim=-1), vt)
+    return o.numpy(), lse.numpy()
+
+
+@pytest.mark.parametrize("shape", [(2, 4, 2, 33, 33, 16), (1, 8, 1, 17, 40, 8), (2, 6, 3, 40, 17, 12),
+                                   (1, 2, 2, 128, 128, 64)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_matches_torch_cpu_fp64(shape, causal):
+    B, H, H_kv, n_q, n_k, d = shape
+    q, k, v = rand((B, H, n_q, d), 71), rand((B, H_kv, n_k, d), 72), rand((B, H_kv, n_k, d), 73)
+    scale = d ** -0.5
+    o, lse = oracle.attention(q, k, v, scale, causal)
+    o_t, lse_t = _torch_reference(q, k, v, scale, causal)
+    fin = np.isfinite(lse_t)
+    if causal and n_q > n_k:
+        # rows with no visible key: torch gives NaN, the oracle's reading is 0 / -inf
+        assert np.all(np.isneginf(lse[~fin])) and np.all(o[~fin] == 0)
+    np.testing.assert_allclose(o[fin], o_t[fin], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse[fin], lse_t[fin], atol=1e-12, rtol=0)
+
+
+def test_matches_torch_sdpa():
+    import torch
+    import torch.nn.functional as F
+    q, k, v = rand((2, 8, 24, 16), 81), rand((2, 2, 24, 16), 82), rand((2, 2, 24, 16), 83)
+    for causal in (False, True):
+        o, _ = oracle.attention(q, k, v, 0.25, causal)
+        ref = F.scaled_dot_product_attention(torch.from_numpy(q), torch.from_numpy(k), torch.from_numpy(v),
+                                             is_causal=causal, scale=0.25, enable_gqa=True).numpy()
+        np.testing.assert_allclose(o, ref, atol=1e-12, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# Brute force on tiny inputs: scalar Python loops with math.exp / math.log.
+# --------------------------------------------------------------------------
+def _brute(q, k, v, scale, causal):
+    B, H, n_q, d = q.shape
+    H_kv, n_k = k.shape[1], k.shape[2]
+    rep = H // H_kv
+    o = np.zeros_like(q)
+    lse = np.zeros((B, H, n_q))
+    for b in range(B):
+        for h in range(H):
+            g = h // rep
+            for i in range(n_q):
+                keys = [j for j in range(n_k) if (not causal) or j <= i + n_k - n_q]
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
+                s = {j: scale * sum(q[b, h, i, t] * k[b, g, j, t] for t in range(d)) for j in keys}
+                m = max(s.values())
+                z = sum(math.exp(s[j] - m) for j in keys)
+                for t in range(d):
+                    o[b, h, i, t] = sum(math.exp(s[j] - m) / z * v[b, g, j, t] for j in keys)
+                lse[b, h, i] = m + math.log(z)
+    return o, lse
+
+
+@pytest.mark.parametrize("shape", [(1, 2, 1, 3, 3, 2), (2, 4, 2, 2, 4, 3), (1, 3, 1, 4, 2, 2)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_brute_force_tiny(shape, causal):
+    B, H, H_kv, n_q, n_k, d = shape
+    q, k, v = rand((B, H, n_q, d), 91), rand((B, H_kv, n_k, d), 92), rand((B, H_kv, n_k, d), 93)
+    o, lse = oracle.attention(q, k, v, 0.77, causal)
+    ob, lb = _brute(q, k, v, 0.77, causal)
+    np.testing.assert_allclose(o, ob, atol=TOL, rtol=0)
+    assert np.array_equal(np.isneginf(lse), np.isneginf(lb))
+    fin = np.isfinite(lb)
+    np.testing.assert_allclose(lse[fin], lb[fin], atol=TOL, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# Storage dtypes: bf16 bits and fp32 are widened exactly.
+# --------------------------------------------------------------------------
+def test_storage_dtypes_widen_exactly():
+    qf = np.random.default_rng(101).standard_normal((1, 2, 9, 8), dtype=np.float32)
+    kf = np.random.default_rng(102).standard_normal((1, 1, 9, 8), dtype=np.float32)
+    vf = np.random.default_rng(103).standard_normal((1, 1, 9, 8), dtype=np.float32)
+    qb, kb, vb = (inputs.f32_to_bf16_bits(x) for x in (qf, kf, vf))
+    o_b, l_b = oracle.attention(qb, kb, vb, 0.5, True)
+    o_w, l_w = oracle.attention(*(inputs.bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb)), 0.5, True)
+    np.testing.assert_array_equal(o_b, o_w)
+    np.testing.assert_array_equal(l_b, l_w)
+    o_f, l_f = oracle.attention(qf, kf, vf, 0.5, True)
+    o_d, l_d = oracle.attention(qf.astype(np.float64), kf.astype(np.float64), vf.astype(np.float64), 0.5, True)
+    np.testing.assert_array_equal(o_f, o_d)
+    np.testing.assert_array_equal(l_f, l_d)
+
+
+def test_row_subset_matches_full():
+    q, k, v = rand((2, 4, 20, 8), 111), rand((2, 2, 20, 8), 112), rand((2, 2, 20, 8), 113)
+    o, lse = oracle.attention(q, k, v, 0.4, True)
+    rows = [(0, 0, 0), (1, 3, 19), (0, 2, 7), (1, 1, 12)]
+    o_r, l_r = oracle.attention_rows(q, k, v, rows, 0.4, True)
+    for n, (b, h, i) in enumerate(rows):
+        np.testing.assert_array_equal(o_r[n], o[b, h, i])
+        assert l_r[n] == lse[b, h, i]
+
+
+# --------------------------------------------------------------------------
+# P-h: decode.  One query per head against the first len_b cache rows equals
+# prefill with N_q = 1 on those rows; padding rows are never read; splitting
+# the keys into S chunks and merging by LSE gives the same result.
+# --------------------------------------------------------------------------
+def test_decode_equals_single_query_prefill_and_split_merge():
+    B, H, H_kv, N_max, d = 3, 4, 2, 50, 8
+    rng = np.random.default_rng(121)
+    q = rng.standard_normal((B, H, d))
+    kc = rng.standard_normal((B, H_kv, N_max, d))
+    vc = rng.standard_normal((B, H_kv, N_max, d))
+    lens = np.array([1, 37, 50], np.int32)
+    for b in range(B):                         # poison the padding
+        kc[b, :, lens[b]:] = np.nan
+        vc[b, :, lens[b]:] = np.nan
+    o, lse = oracle.decode(q, kc, vc, lens, 0.35)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    for b in range(B):
+        L = int(lens[b])
+        op, lp = oracle.attention(q[b][None, :, None, :], kc[b:b + 1, :, :L], vc[b:b + 1, :, :L], 0.35, False)
+        np.testing.assert_array_equal(o[b], op[0, :, 0])
+        np.testing.assert_array_equal(lse[b], lp[0, :, 0])
+        for h in range(H):
+            g = h // (H // H_kv)
+            for S in (1, 2, 16, 64):
+                oc, lc = online.split_partials(q[b, h], kc[b, g, :L], vc[b, g, :L], 0.35, S)
+                om, lm = online.merge_partials(oc, lc)
+                np.testing.assert_allclose(om, o[b, h], atol=TOL, rtol=0)
+                assert abs(lm - lse[b, h]) <= TOL
+
+
+def test_decode_rejects_bad_lengths():
+    q = rand((2, 2, 4), 1)
+    kc = rand((2, 1, 5, 4), 2)
+    with pytest.raises(ValueError):
+        oracle.decode(q, kc, kc, [0, 3], 1.0)
+    with pytest.raises(ValueError):
+        oracle.decode(q, kc, kc, [6, 3], 1.0)
