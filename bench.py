@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * prefill: fa_fwd on the MHA workload B=8, H=H_kv=32, N=2048, d=128, causal,
+    bf16 (the headline: attention TFLOP/s, FLOPs = 4*B*H*N_q*N_k*d halved for
+    causal);
+  * decode: fa_decode on the GQA decode workload B=32, H=32, H_kv=8, d=128,
+    seq lens uniform in [8192, 32768], 16 splits (KV-read GB/s).
+Inputs are resident in HBM before the timed region; outputs are preallocated.
+Each launch is bracketed by HIP events recorded on the stream it runs on.
+
+Prints ONE JSON line.  ``--workload`` swaps the prefill workload for another
+named one (for exploration; the headline is the default).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mha", choices=["mha", "gqa", "mqa"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
+                    help="time one half of the step only (for profiling runs)")
+    return ap.parse_args()
+
+
+def kernel_source_hash(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "transformer_attention_fa_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel_key, src_files):
+    """HBM traffic per launch from committed rocprofv3 --pmc summaries, or None
+    when the kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path)).get(kernel_key)
+    except (ValueError, OSError):
+        return None
+    if not rec or rec.get("source_hash") != kernel_source_hash(src_files):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(spec, n_batches):
+    """The fp64 oracle on a bounded sample (the first n_batches sequences) of the
+    prefill workload, timed on the host cores."""
+    import oracle
+    from transformer_attention_fa_amd import inputs, roofline
+    import dataclasses
+    sub = dataclasses.replace(spec, B=n_batches)
+    data = inputs.prefill_inputs(sub)
+    t0 = time.perf_counter()
+    oracle.attention(data.q, data.k, data.v, sub.scale, sub.causal)
+    dt = time.perf_counter() - t0
+    flops = roofline.attention_flops(sub.B, sub.H, sub.N_q, sub.N_k, sub.d, sub.causal)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"{n_batches} of {spec.B} sequences ({n_batches * spec.H} heads) of {spec.name}, "
+                      f"fp64, {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(each GPU would run its own shard of heads or sequences; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from transformer_attention_fa_amd import api, inputs, roofline
+
+    api.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pspec = {"mha": inputs.MHA_PREFILL, "gqa": inputs.GQA_PREFILL, "mqa": inputs.MQA_PREFILL}[args.workload]
+    dspec = inputs.GQA_DECODE
+    do_prefill = args.only in (None, "prefill")
+    do_decode = args.only in (None, "decode")
+
+    def dev_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if do_prefill:
+        pdata = inputs.prefill_inputs(pspec)
+        q, k, v = (dev_bf16(x) for x in (pdata.q, pdata.k, pdata.v))
+        del pdata
+        o = torch.empty_like(q)
+        lse = torch.empty((pspec.B, pspec.H, pspec.N_q), dtype=torch.float32, device=dev)
+    if do_decode:
+        ddata = inputs.decode_inputs(dspec)
+        dq = dev_bf16(ddata.q)
+        kc, vc = dev_bf16(ddata.k_cache), dev_bf16(ddata.v_cache)
+        lens = torch.from_numpy(ddata.seq_lens).to(dev)
+        seq_lens = ddata.seq_lens.copy()
+        del ddata
+        d_o = torch.empty_like(dq)
+        d_lse = torch.empty((dspec.B, dspec.H), dtype=torch.float32, device=dev)
+        ws = torch.empty(api.decode_workspace_bytes(dspec.B, dspec.H, dspec.d, dspec.num_splits),
+                         dtype=torch.uint8, device=dev)
+
+    def step(ev=None):
+        if do_prefill:
+            if ev is not None:
+                ev[0].record()
+            api.fwd(q, k, v, causal=pspec.causal, scale=pspec.scale, out=o, lse=lse)
+            if ev is not None:
+                ev[1].record()
+        if do_decode:
+            if ev is not None:
+                ev[2].record()
+            api.decode(dq, kc, vc, lens, num_splits=dspec.num_splits, scale=dspec.scale,
+                       out=d_o, lse=d_lse, workspace=ws)
+            if ev is not None:
+                ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)"}
+    config = {"workload": "", "prefill": None, "decode": None}
+    if do_prefill:
+        t_pf = [e[0].elapsed_time(e[1]) for e in events]        # ms
+        t_avg = float(np.mean(t_pf))
+        flops = pspec.flops()
+        tflops = flops / (t_avg * 1e-3) / 1e12
+        traffic = traffic_for(f"fwd_bf16:{pspec.name}", ["fwd_bf16.hip"])
+        rec.update({"value": tflops, "unit": "TFLOP/s"})
+        rec["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": roofline.PEAK_BF16_TFLOPS,
+                           "unit": "TFLOP/s", "frac": tflops / roofline.PEAK_BF16_TFLOPS, "traffic": traffic,
+                           "kernel": "fwd_bf16_kernel", "launch_ms_avg": t_avg, "launch_ms_min": float(np.min(t_pf)),
+                           "flop_per_launch": flops}
+        config["workload"] = pspec.name
+        config["prefill"] = {"B": pspec.B, "H": pspec.H, "H_kv": pspec.H_kv, "N_q": pspec.N_q, "N_k": pspec.N_k,
+                             "d": pspec.d, "causal": pspec.causal, "seed": pspec.seed}
+    if do_decode:
+        t_dc = [e[2].elapsed_time(e[3]) for e in events]
+        t_avg_d = float(np.mean(t_dc))
+        kv_bytes = roofline.decode_kv_bytes(dspec.H_kv, dspec.d, seq_lens)
+        gbps = kv_bytes / (t_avg_d * 1e-3) / 1e9
+        rec["decode"] = {"value": gbps, "unit": "GB/s", "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS,
+                         "ms_avg": t_avg_d, "ms_min": float(np.min(t_dc)), "kv_bytes": kv_bytes,
+                         "roofline": {"bound": "hbm", "achieved": gbps, "peak": roofline.PEAK_HBM_GBPS,
+                                      "unit": "GB/s", "frac": gbps / roofline.PEAK_HBM_GBPS,
+                                      "traffic": traffic_for(f"decode:{dspec.name}", ["decode.hip"]),
+                                      "kernel": "decode_split_kernel + decode_combine_kernel"}}
+        config["workload"] = (config["workload"] + " + " if config["workload"] else "") + dspec.name
+        config["decode"] = {"B": dspec.B, "H": dspec.H, "H_kv": dspec.H_kv, "d": dspec.d,
+                            "seq_len_range": [dspec.len_lo, dspec.len_hi], "num_splits": dspec.num_splits,
+                            "seed": dspec.seed}
+        if not do_prefill:
+            rec.update({"value": gbps, "unit": "GB/s"})
+    rec["config"] = config
+    if do_prefill and not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(pspec, n_batches=max(1, min(pspec.B, 4)))
+    props = torch.cuda.get_device_properties(dev)
+    rec["device"] = {"name": props.name, "cus": props.multi_processor_count,
+                     "gcn_arch": getattr(props, "gcnArchName", "")}
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
+ *
+ * The library computes attention forward, O = softmax(scale * Q K^T + mask) V,
+ * and the per-row log-sum-exp, without ever storing the N_q x N_k score
+ * matrix: keys and values are streamed through on-chip memory in tiles and the
+ * softmax is carried as a running maximum and running sum per query row.  It
+ * also runs one decode step (one new query per head) against a KV cache, with
+ * the keys of each sequence split into chunks whose partial results are merged
+ * by their log-sum-exp.
+ *
+ * Sources, by web page title and section:
+ *  [AV] "Attention variants: GQA/MQA/FlashAttention" (youngju.dev)
+ *       §1 cost model (B, H, N, d_k; the (B,H,N,N) score tensor),
+ *       §2 MQA/GQA and the gqa_attention snippet (q [B,H,N,d_k], k/v [B,G,N,d_k],
+ *          rep = H/G, repeat_interleave on the head axis, scores / sqrt(d_k)),
+ *       §3 FlashAttention tiling and online softmax (exact, not approximate),
+ *       §5.5 causal block skip, §7 decode is memory-bandwidth bound,
+ *       troubleshooting list: H must be a multiple of G.
+ *  [ME] "Attention mechanism evolution: MHA -> MLA, Flash Attention" (toolsku.com)
+ *       MHA/GQA module code (head_dim^-0.5 scale, -inf mask fill, KV cache
+ *       concatenated on the sequence axis, _repeat_kv over contiguous heads),
+ *       Flash Attention usage box (flash_attn_func(q, k, v, causal,
+ *       softmax_scale=None) with None meaning 1/sqrt(d)).
+ *
+ * Conventions shared by every entry point
+ *  - Layout: row-major, head dimension fastest.  q [B,H,N_q,d];
+ *    k, v [B,H_kv,N_k,d]; o [B,H,N_q,d]; lse [B,H,N_q] (fp32).  Decode:
+ *    q [B,H,d]; k_cache, v_cache [B,H_kv,N_max,d]; o [B,H,d]; lse [B,H].
+ *  - Head sharing [AV §2, ME GQA code]: query head h reads key/value head
+ *    g = h / (H / H_kv).  H_kv == H is MHA, H_kv == 1 is MQA.  H must be a
+ *    multiple of H_kv.
+ *  - Causal mask (causal != 0) [AV §5.5, ME MHA code]: query row i sees key j
+ *    iff j <= i + (N_k - N_q) (aligned to the bottom-right corner, so a block
+ *    of new queries after a cache sees the whole cache; with N_q == N_k this is
+ *    j <= i).  A row that sees no key gets o = 0 and lse = -inf.
+ *  - lse = ln(sum_visible exp(s_ij)) with s_ij = scale * <q_i, k_j>: natural
+ *    log, in units of the scaled scores.
+ *  - scale must be finite and >= 0 (the pages use 1/sqrt(d)); a negative scale
+ *    returns FA_ERR_UNSUPPORTED.
+ *  - Supported head dimensions: d = 64 and d = 128 (others: FA_ERR_UNSUPPORTED).
+ *  - Pointers are device pointers (HIP), 16-byte aligned (lse: 4-byte aligned),
+ *    owned by the caller; the library never allocates, frees or keeps them.
+ *    Inputs and outputs must not overlap.
+ *  - Calls are asynchronous: they validate on the host, enqueue kernels on
+ *    `stream` and return.  No host synchronisation; results are visible after
+ *    the stream is synchronised.  Calls on different streams may run at once.
+ *  - Errors: invalid arguments are rejected on the host before any launch
+ *    (FA_ERR_INVALID_ARGUMENT / FA_ERR_UNSUPPORTED) and nothing is written.
+ *    A failed launch returns FA_ERR_HIP.  fa_last_error() gives a message for
+ *    the calling thread's last failure.  Nothing throws across the ABI.
+ *  - Thread safety: no global mutable state besides the per-thread message.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_INVALID_ARGUMENT = 1,
+    FA_ERR_UNSUPPORTED = 2,
+    FA_ERR_HIP = 3
+} fa_status_t;
+
+/*
+ * fa_fwd -- attention forward, bf16 in / bf16 out, fp32 accumulation.
+ * [AV §3 tiling + online softmax; AV §2 / ME GQA head sharing; AV §5.5 causal]
+ *   q      [B,H,N_q,d]   bf16, device
+ *   k, v   [B,H_kv,N_k,d] bf16, device
+ *   o      [B,H,N_q,d]   bf16, device, written (rounded to nearest even)
+ *   lse    [B,H,N_q]     fp32, device, written; may be NULL (not written)
+ *   B, H, H_kv, N_q, N_k >= 1; H % H_kv == 0; d in {64, 128}
+ *   scale  softmax scale applied to q.k (e.g. 1/sqrt(d)); finite, >= 0
+ *   causal 0 = no mask, non-zero = bottom-right causal mask
+ *   stream HIP stream to enqueue on (0 = the null stream)
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int N_q, int N_k, int d,
+                   float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_fwd_f32 -- the same operation with fp32 inputs and fp32 output
+ * (fp32 arithmetic throughout).  Arguments and semantics as fa_fwd.
+ */
+fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                       int B, int H, int H_kv, int N_q, int N_k, int d,
+                       float scale, int causal, hipStream_t stream);
+
+/*
+ * fa_decode_workspace_bytes -- size of the workspace fa_decode needs:
+ * fp32 partial outputs [B,H,num_splits,d] followed by fp32 partial
+ * log-sum-exps [B,H,num_splits].  Returns 0 for invalid arguments.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * fa_decode -- one decode step: each sequence b has one new query per head,
+ * attending without a mask to the first seq_lens[b] rows of its cache
+ * [ME KV-cache code: the cache grows along the sequence axis; AV §7 decode
+ * re-reads the cache].  The keys of sequence b are cut into num_splits chunks
+ * of ceil(seq_lens[b] / num_splits) rows; one kernel computes each chunk's
+ * partial output and log-sum-exp, a second merges them:
+ *   M = max_c lse_c;  lse = M + ln sum_c exp(lse_c - M);
+ *   o = sum_c exp(lse_c - lse) o_c.
+ * (The merge is not on the pages; it is the online-softmax rescale of AV §3
+ * applied to whole-chunk summaries.)  Empty chunks contribute nothing.
+ *   q         [B,H,d]          bf16, device
+ *   k_cache   [B,H_kv,N_max,d] bf16, device; rows >= seq_lens[b] are never read
+ *   v_cache   [B,H_kv,N_max,d] bf16, device; same
+ *   seq_lens  [B] int32, device; each value must lie in 1..N_max (trusted:
+ *             the library does not read device memory on the host)
+ *   o         [B,H,d] bf16, device, written
+ *   lse       [B,H]   fp32, device, written; may be NULL
+ *   B, H, H_kv, N_max >= 1; H % H_kv == 0; d in {64, 128}
+ *   scale     finite, >= 0
+ *   num_splits 1 .. 256
+ *   workspace device buffer of at least fa_decode_workspace_bytes(B,H,d,num_splits)
+ *             bytes, 16-byte aligned, owned by the caller; its contents on
+ *             entry are ignored and on return are unspecified
+ *   stream    HIP stream; both kernels are enqueued on it, in order
+ */
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seq_lens, void* o, float* lse,
+                      int B, int H, int H_kv, int N_max, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(fa_status_t s);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

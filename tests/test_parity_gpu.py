@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Small problems are compared element by element over the whole output; they
+span several query and key tiles and end in ragged tails.  The full-size
+workloads run in the launch configuration the benchmark times and are compared
+on sampled rows (the oracle computes rows one by one) plus a whole-tensor
+property: every output row is a convex combination of value rows.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import (BF16_LSE_REL_TOL, BF16_O_TOL, F32_TOL, bf16_to_device, compare, f32_to_device,
+                            say, to_f64)
+from transformer_attention_fa_amd import api, inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu(require_gpu):
+    api.load()
+
+
+def _spec(B, H, H_kv, N_q, N_k, d, causal, dtype="bf16", seed=7, k_scale=1.0):
+    name = f"B{B}_H{H}_Hkv{H_kv}_Nq{N_q}_Nk{N_k}_d{d}_{'causal' if causal else 'full'}_{dtype}"
+    return inputs.Prefill(name, B, H, H_kv, N_q, N_k, d, causal, dtype, seed, k_scale)
+
+
+def _run_fwd(data):
+    s = data.spec
+    if s.dtype == "bf16":
+        q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+        o, lse = api.fwd(q, k, v, causal=s.causal, scale=s.scale)
+    else:
+        q, k, v = (f32_to_device(x) for x in (data.q, data.k, data.v))
+        o, lse = api.fwd_f32(q, k, v, causal=s.causal, scale=s.scale)
+    import torch
+    torch.cuda.synchronize()
+    return o, lse
+
+
+SMALL_BF16 = [
+    (1, 2, 2, 300, 300, 128, False),
+    (1, 2, 2, 300, 300, 128, True),
+    (2, 8, 2, 200, 333, 128, True),      # GQA, N_q < N_k: bottom-right causal
+    (2, 8, 2, 200, 333, 128, False),
+    (1, 4, 1, 129, 64, 64, False),       # MQA, d = 64
+    (1, 4, 1, 129, 64, 64, True),        # N_q > N_k: leading rows see no key
+    (1, 3, 3, 1, 1, 128, False),
+    (1, 3, 1, 1, 17, 128, True),
+    (2, 4, 4, 517, 517, 64, True),
+    (1, 2, 1, 1000, 1000, 128, True),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL_BF16, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_bf16_small_full_compare(shape):
+    spec = _spec(*shape)
+    say(f"fa_fwd bf16 {spec.name}")
+    data = inputs.prefill_inputs(spec)
+    o, lse = _run_fwd(data)
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, spec.causal)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+def test_fwd_bf16_sharp_softmax():
+    """K scaled by 4: scores ~ N(0, 16); rows are nearly one-hot."""
+    spec = _spec(1, 4, 2, 256, 256, 128, True, k_scale=4.0)
+    data = inputs.prefill_inputs(spec)
+    o, lse = _run_fwd(data)
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, spec.causal)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label="sharp")
+
+
+SMALL_F32 = [
+    inputs.SINGLE_HEAD_F32,
+    inputs.SINGLE_HEAD_F32_CAUSAL,
+    _spec(2, 4, 2, 77, 190, 128, True, dtype="f32"),
+    _spec(2, 4, 2, 190, 77, 128, True, dtype="f32"),
+    _spec(1, 6, 3, 100, 300, 64, False, dtype="f32"),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL_F32, ids=lambda s: s.name)
+def test_fwd_f32_full_compare(spec):
+    say(f"fa_fwd_f32 {spec.name}")
+    data = inputs.prefill_inputs(spec)
+    o, lse = _run_fwd(data)
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, spec.causal)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, F32_TOL, F32_TOL, lse_relative=False, label=spec.name)
+
+
+def _sample_rows(spec, n_heads=6, n_random=24, seed=0):
+    rng = np.random.default_rng(seed)
+    heads = {(0, 0), (spec.B - 1, spec.H - 1)}
+    while len(heads) < min(n_heads, spec.B * spec.H):
+        heads.add((int(rng.integers(spec.B)), int(rng.integers(spec.H))))
+    fixed = [0, 1, 31, 32, 63, 64, 127, 128, 255, 256, spec.N_q // 2, spec.N_q - 2, spec.N_q - 1]
+    rows = []
+    for b, h in sorted(heads):
+        idx = {i for i in fixed if 0 <= i < spec.N_q}
+        idx |= set(int(x) for x in rng.integers(0, spec.N_q, n_random))
+        rows += [(b, h, i) for i in sorted(idx)]
+    return np.array(rows, dtype=np.int64)
+
+
+def _convex_hull_check(o, v, spec):
+    """Each output row is a convex combination of (visible) value rows of its KV head:
+    per element, min_j V <= O <= max_j V, up to bf16 output rounding."""
+    import torch
+    rep = spec.H // spec.H_kv
+    vf = v.float()
+    vmax = vf.amax(dim=2).repeat_interleave(rep, dim=1)[:, :, None, :]
+    vmin = vf.amin(dim=2).repeat_interleave(rep, dim=1)[:, :, None, :]
+    of = o.float()
+    slack = 2.0 ** -7 * torch.maximum(vmax.abs(), vmin.abs()) + 1e-6
+    assert bool(torch.isfinite(of).all())
+    assert bool((of <= vmax + slack).all()) and bool((of >= vmin - slack).all())
+
+
+@pytest.mark.parametrize("spec", [inputs.MHA_PREFILL, inputs.GQA_PREFILL, inputs.MQA_PREFILL], ids=lambda s: s.name)
+def test_fwd_bf16_workloads_sampled(spec):
+    say(f"fa_fwd bf16 full-size workload {spec.name}")
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    o, lse = api.fwd(q, k, v, causal=spec.causal, scale=spec.scale)
+    import torch
+    torch.cuda.synchronize()
+    _convex_hull_check(o, v, spec)
+    rows = _sample_rows(spec)
+    o_ref, lse_ref = oracle.attention_rows(data.q, data.k, data.v, rows, spec.scale, spec.causal)
+    o_all, lse_all = to_f64(o), to_f64(lse)
+    o_gpu = o_all[rows[:, 0], rows[:, 1], rows[:, 2]]
+    lse_gpu = lse_all[rows[:, 0], rows[:, 1], rows[:, 2]]
+    assert np.all(np.isfinite(lse_all))
+    compare(o_gpu, lse_gpu, o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"{spec.name} ({len(rows)} rows)")
+
+
+def test_fwd_zero_query_closed_form():
+    """Q = 0: every visible key has equal weight, o_i = mean(V[0..i]) (causal), lse_i = ln(i+1)."""
+    import torch
+    spec = _spec(1, 2, 1, 300, 300, 128, True)
+    data = inputs.prefill_inputs(spec)
+    q = torch.zeros((1, 2, 300, 128), dtype=torch.bfloat16, device="cuda")
+    k, v = bf16_to_device(data.k), bf16_to_device(data.v)
+    o, lse = api.fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    vv = inputs.bf16_bits_to_f32(data.v).astype(np.float64)[0, 0]
+    mean = np.cumsum(vv, axis=0) / np.arange(1, 301)[:, None]
+    ref_o = np.broadcast_to(mean, (2, 300, 128))
+    ref_lse = np.broadcast_to(np.log(np.arange(1, 301)), (2, 300))
+    compare(to_f64(o)[0], to_f64(lse)[0], ref_o, ref_lse, BF16_O_TOL, BF16_LSE_REL_TOL, label="Q=0")
+
+
+def test_fwd_deterministic_and_no_out_of_bounds_writes():
+    import torch
+    spec = _spec(2, 4, 2, 333, 333, 128, True)
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    n_o, n_l, G = q.numel(), 2 * 4 * 333, 4096
+    o_buf = torch.full((n_o + 2 * G,), 7.0, dtype=torch.bfloat16, device="cuda")
+    l_buf = torch.full((n_l + 2 * G,), 7.0, dtype=torch.float32, device="cuda")
+    o = o_buf[G:G + n_o].view(q.shape)
+    lse = l_buf[G:G + n_l].view(2, 4, 333)
+    api.fwd(q, k, v, causal=True, out=o, lse=lse)
+    first_o, first_l = o.clone(), lse.clone()
+    api.fwd(q, k, v, causal=True, out=o, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(o, first_o) and torch.equal(lse, first_l)
+    assert bool((o_buf[:G] == 7.0).all()) and bool((o_buf[G + n_o:] == 7.0).all())
+    assert bool((l_buf[:G] == 7.0).all()) and bool((l_buf[G + n_l:] == 7.0).all())
+
+
+def test_fwd_without_lse():
+    import torch
+    spec = _spec(1, 2, 2, 128, 128, 128, False)
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    o1, _ = api.fwd(q, k, v)
+    o2, l2 = api.fwd(q, k, v, lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)
+
+
+# ------------------------------------------------------------------ decode
+def _decode_run(data, num_splits):
+    import torch
+    s = data.spec
+    q = bf16_to_device(data.q)
+    kc, vc = bf16_to_device(data.k_cache), bf16_to_device(data.v_cache)
+    lens = torch.from_numpy(data.seq_lens).cuda()
+    o, lse = api.decode(q, kc, vc, lens, num_splits=num_splits, scale=s.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def test_decode_workload_full_compare():
+    spec = inputs.GQA_DECODE
+    say(f"fa_decode full-size workload {spec.name}")
+    data = inputs.decode_inputs(spec)           # padding rows hold NaN
+    o, lse = _decode_run(data, spec.num_splits)
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+def _small_decode_spec(H=8, H_kv=2, d=128, N_max=3000, B=6, seed=11):
+    return inputs.Decode(f"decode_B{B}_H{H}_Hkv{H_kv}_d{d}", B, H, H_kv, d, 1, N_max, N_max, 16, seed)
+
+
+@pytest.mark.parametrize("num_splits", [1, 4, 16, 64, 256])
+def test_decode_split_counts_and_edge_lengths(num_splits):
+    spec = _small_decode_spec()
+    lens = np.array([1, 2, 15, 16, 17, 3000], np.int32)      # shorter than the split count, and N_max
+    data = inputs.decode_inputs(spec, seq_lens=lens)          # rows past each length hold NaN
+    o, lse = _decode_run(data, num_splits)
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"S={num_splits}")
+
+
+@pytest.mark.parametrize("H,H_kv,d", [(16, 1, 64), (12, 4, 128), (8, 8, 128), (64, 8, 128)])
+def test_decode_head_sharing(H, H_kv, d):
+    spec = _small_decode_spec(H=H, H_kv=H_kv, d=d, N_max=1200, B=3, seed=13)
+    data = inputs.decode_inputs(spec)
+    o, lse = _decode_run(data, 8)
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+def test_decode_deterministic():
+    import torch
+    spec = _small_decode_spec(seed=17)
+    data = inputs.decode_inputs(spec)
+    o1, l1 = _decode_run(data, 16)
+    o2, l2 = _decode_run(data, 16)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)

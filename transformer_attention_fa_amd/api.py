@@ -1,0 +1,185 @@
+"""Thin Python binding of libfa.so (include/fa.h) over ctypes.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch is used for device memory and for the
+current stream; there is no CPU or PyTorch fallback -- if libfa.so is missing
+or a call fails, an exception is raised.
+
+Entry points mirror the C names: ``fwd`` (fa_fwd, bf16), ``fwd_f32``
+(fa_fwd_f32), ``decode`` (fa_decode), ``decode_workspace_bytes``.
+``scale=None`` means 1/sqrt(d), like the ``softmax_scale=None`` default of the
+flash_attn_func usage shown in "Attention mechanism evolution: MHA -> MLA,
+Flash Attention" (toolsku.com), Flash Attention section.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
+
+EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes",
+            "fa_status_string", "fa_last_error")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(message)
+        self.status = status
+
+
+def load():
+    """Open libfa.so (built in-tree) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise FileNotFoundError(
+            f"{LIB_PATH} is not built; run `python -m transformer_attention_fa_amd.build` "
+            "(there is no fallback path)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_f32.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error.argtypes = []
+    lib.fa_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def check(status: int) -> None:
+    if status != FA_OK:
+        lib = load()
+        raise FAError(status, f"{lib.fa_status_string(status).decode()}: {lib.fa_last_error().decode()}")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _require(t, name, dtype, ndim, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major, d fastest)")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _fwd(fn, dtype, q, k, v, causal, scale, out, lse):
+    torch = _torch()
+    _require(q, "q", dtype, 4)
+    _require(k, "k", dtype, 4, q.device)
+    _require(v, "v", dtype, 4, q.device)
+    B, H, N_q, d = q.shape
+    Bk, H_kv, N_k, dk = k.shape
+    if Bk != B or dk != d or tuple(v.shape) != tuple(k.shape):
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)}, k {tuple(k.shape)}, v {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", dtype, 4, q.device)
+        if tuple(out.shape) != tuple(q.shape):
+            raise ValueError("out must have the shape of q")
+    if lse is None:
+        lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
+    elif lse is not False:
+        _require(lse, "lse", torch.float32, 3, q.device)
+        if tuple(lse.shape) != (B, H, N_q):
+            raise ValueError("lse must have shape [B, H, N_q]")
+    lse_t = None if lse is False else lse
+    with torch.cuda.device(q.device):
+        check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse_t),
+                 B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)), _stream(q.device)))
+    return out, lse_t
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fa_fwd: bf16 q [B,H,N_q,d], k/v [B,H_kv,N_k,d] -> (o bf16 [B,H,N_q,d], lse fp32 [B,H,N_q]).
+
+    Pass ``lse=False`` to skip the log-sum-exp output.
+    """
+    torch = _torch()
+    return _fwd(load().fa_fwd, torch.bfloat16, q, k, v, causal, scale, out, lse)
+
+
+def fwd_f32(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+    """fa_fwd_f32: the same with fp32 tensors."""
+    torch = _torch()
+    return _fwd(load().fa_fwd_f32, torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
+    return int(load().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def decode(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | None = None,
+           out=None, lse=None, workspace=None):
+    """fa_decode: q [B,H,d], caches [B,H_kv,N_max,d] (bf16), seq_lens [B] int32 on the device.
+
+    Returns (o bf16 [B,H,d], lse fp32 [B,H]).  ``workspace`` (uint8 tensor) may
+    be passed to avoid an allocation per call.
+    """
+    torch = _torch()
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_cache, "k_cache", torch.bfloat16, 4, q.device)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, q.device)
+    _require(seq_lens, "seq_lens", torch.int32, 1, q.device)
+    B, H, d = q.shape
+    Bk, H_kv, N_max, dk = k_cache.shape
+    if Bk != B or dk != d or tuple(v_cache.shape) != tuple(k_cache.shape) or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        # need == 0 means the arguments are invalid: the library call below reports why
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, 3, q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    elif lse is not False:
+        _require(lse, "lse", torch.float32, 2, q.device)
+    lse_t = None if lse is False else lse
+    with torch.cuda.device(q.device):
+        check(load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                               out.data_ptr(), _ptr(lse_t), B, H, H_kv, N_max, d, float(scale),
+                               int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    return out, lse_t

@@ -1,0 +1,141 @@
+// fa_api.cpp -- the C ABI declared in include/fa.h: argument validation on the
+// host, then kernel launches on the caller's stream.  No allocation, no host
+// synchronisation, no exceptions across the boundary.
+#include "fa.h"
+#include "fa_internal.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+fa_status_t fail(fa_status_t s, const char* fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool aligned(const void* p, std::uintptr_t n) { return (reinterpret_cast<std::uintptr_t>(p) % n) == 0; }
+
+// Element counts stay far below 2^62; the kernels index with 64-bit offsets.
+bool too_large(long long a, long long b, long long c, long long d)
+{
+    const long long lim = 1LL << 40;
+    return a * b > lim || a * b * c > lim || a * b * c * d > lim;
+}
+
+fa_status_t check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         int B, int H, int H_kv, int N_q, int N_k, int d, float scale)
+{
+    if (!q || !k || !v || !o)
+        return fail(FA_ERR_INVALID_ARGUMENT, "null q, k, v or o pointer");
+    if (B < 1 || H < 1 || H_kv < 1 || N_q < 1 || N_k < 1 || d < 1)
+        return fail(FA_ERR_INVALID_ARGUMENT, "sizes must be >= 1 (B=%d H=%d H_kv=%d N_q=%d N_k=%d d=%d)",
+                    B, H, H_kv, N_q, N_k, d);
+    if (H % H_kv != 0)
+        return fail(FA_ERR_INVALID_ARGUMENT, "H=%d is not a multiple of H_kv=%d", H, H_kv);
+    if (d != 64 && d != 128)
+        return fail(FA_ERR_UNSUPPORTED, "head dimension d=%d not supported (64 or 128)", d);
+    if (!std::isfinite(scale))
+        return fail(FA_ERR_INVALID_ARGUMENT, "scale must be finite");
+    if (scale < 0.0f)
+        return fail(FA_ERR_UNSUPPORTED, "negative scale not supported");
+    if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(o, 16))
+        return fail(FA_ERR_INVALID_ARGUMENT, "q, k, v and o must be 16-byte aligned");
+    if (lse && !aligned(lse, 4))
+        return fail(FA_ERR_INVALID_ARGUMENT, "lse must be 4-byte aligned");
+    if (too_large(B, H, N_q, d) || too_large(B, H_kv, N_k, d))
+        return fail(FA_ERR_UNSUPPORTED, "problem too large");
+    return FA_OK;
+}
+
+fa_status_t from_hip(hipError_t e, const char* what)
+{
+    if (e == hipSuccess) return FA_OK;
+    return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status_t s)
+{
+    switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARGUMENT: return "FA_ERR_INVALID_ARGUMENT";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+    }
+    return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error(void) { return g_last_error; }
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int H_kv, int N_q, int N_k, int d,
+                   float scale, int causal, hipStream_t stream)
+{
+    fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
+    if (s != FA_OK) return s;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0};
+    return from_hip(fa::launch_fwd_bf16(a, stream), "fa_fwd launch");
+}
+
+fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                       int B, int H, int H_kv, int N_q, int N_k, int d,
+                       float scale, int causal, hipStream_t stream)
+{
+    fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
+    if (s != FA_OK) return s;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0};
+    return from_hip(fa::launch_fwd_f32(a, stream), "fa_fwd_f32 launch");
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits)
+{
+    if (B < 1 || H < 1 || d < 1 || num_splits < 1 || num_splits > 256) return 0;
+    if (too_large(B, H, num_splits, d + 1)) return 0;
+    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
+    size_t o_bytes = rows * (size_t)d * sizeof(float);
+    o_bytes = (o_bytes + 255) / 256 * 256;           // partial lse starts 256-byte aligned
+    return o_bytes + rows * sizeof(float);
+}
+
+fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
+                      const int* seq_lens, void* o, float* lse,
+                      int B, int H, int H_kv, int N_max, int d, float scale,
+                      int num_splits, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream)
+{
+    fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
+    if (s != FA_OK) return s;
+    if (!seq_lens)
+        return fail(FA_ERR_INVALID_ARGUMENT, "null seq_lens");
+    if (!aligned(seq_lens, 4))
+        return fail(FA_ERR_INVALID_ARGUMENT, "seq_lens must be 4-byte aligned");
+    if (num_splits < 1 || num_splits > 256)
+        return fail(FA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..256", num_splits);
+    if (!workspace || !aligned(workspace, 16))
+        return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 16-byte aligned");
+    size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
+    if (need == 0 || workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
+    size_t o_bytes = (rows * (size_t)d * sizeof(float) + 255) / 256 * 256;
+    fa::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse,
+                     static_cast<float*>(workspace),
+                     reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes),
+                     B, H, H_kv, N_max, d, num_splits, scale};
+    return from_hip(fa::launch_decode(a, stream), "fa_decode launch");
+}
+
+}  // extern "C"

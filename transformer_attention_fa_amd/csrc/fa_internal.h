@@ -1,0 +1,41 @@
+// fa_internal.h -- launch interface between the C-ABI layer (fa_api.cpp) and
+// the gfx950 kernels.  Arguments reaching these functions are already
+// validated; each returns the hipError_t of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace fa {
+
+// One prefill problem, as validated by fa_fwd / fa_fwd_f32.
+struct FwdArgs {
+    const void* q;       // [B,H,N_q,d]
+    const void* k;       // [B,H_kv,N_k,d]
+    const void* v;       // [B,H_kv,N_k,d]
+    void* o;             // [B,H,N_q,d]
+    float* lse;          // [B,H,N_q] or nullptr
+    int B, H, H_kv, N_q, N_k, d;
+    float scale;         // softmax scale on q.k
+    int causal;
+};
+
+// One decode step, as validated by fa_decode.
+struct DecodeArgs {
+    const void* q;       // [B,H,d]
+    const void* k;       // [B,H_kv,N_max,d]
+    const void* v;       // [B,H_kv,N_max,d]
+    const int* seq_lens; // [B], device
+    void* o;             // [B,H,d]
+    float* lse;          // [B,H] or nullptr
+    float* part_o;       // [B,H,S,d]  workspace
+    float* part_lse;     // [B,H,S]    workspace
+    int B, H, H_kv, N_max, d, num_splits;
+    float scale;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa

@@ -181,13 +181,16 @@ def decode_seq_lens(spec: Decode) -> np.ndarray:
     return rng.integers(spec.len_lo, spec.len_hi, size=spec.B, endpoint=True).astype(np.int32)
 
 
-def decode_inputs(spec: Decode, pad: int | None = BF16_QNAN) -> DecodeData:
+def decode_inputs(spec: Decode, pad: int | None = BF16_QNAN, seq_lens=None) -> DecodeData:
     """q, the two caches and seq_lens for a decode workload (bf16 storage).
 
     ``pad`` is the bf16 bit pattern written to cache rows at or beyond len_b
-    (quiet NaN by default; None leaves zeros).
+    (quiet NaN by default; None leaves zeros).  ``seq_lens`` overrides the
+    drawn lengths (each in 1..N_max).
     """
-    lens = decode_seq_lens(spec)
+    lens = decode_seq_lens(spec) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    if lens.shape != (spec.B,) or lens.min() < 1 or lens.max() > spec.N_max:
+        raise ValueError("seq_lens must hold B values in 1..N_max")
     q = f32_to_bf16_bits(np.random.default_rng([spec.seed, 0]).standard_normal((spec.B, spec.H, spec.d),
                                                                               dtype=np.float32))
     caches = []
