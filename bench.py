@@ -35,8 +35,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mha", choices=["mha", "gqa", "mqa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode"], default=None,
-                    help="time one half of the step only (for profiling runs)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="time one half of the step only (for profiling runs); 'copy' runs a plain "
+                         "1 GiB device-to-device copy, the reference for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -94,6 +95,15 @@ def main():
     api.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.warmup + args.steps}))
+        return
     pspec = {"mha": inputs.MHA_PREFILL, "gqa": inputs.GQA_PREFILL, "mqa": inputs.MQA_PREFILL}[args.workload]
     dspec = inputs.GQA_DECODE
     do_prefill = args.only in (None, "prefill")

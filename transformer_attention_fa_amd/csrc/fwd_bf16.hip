@@ -3,35 +3,55 @@
 // Method ("Attention variants: GQA/MQA/FlashAttention" (youngju.dev) §3):
 // cut Q into blocks (one per workgroup) and K/V into blocks streamed through
 // LDS; per query row keep a running maximum m and running sum l; for each key
-// block compute the block scores, raise m, bring the accumulator and l to the
-// new m, add the block's exp(S - m) V; divide by l at the end.  Causal
-// problems skip key blocks wholly in the future and mask inside the diagonal
-// blocks (§5.5 of the same page).  Query head h reads KV head h / (H / H_kv)
-// (§2 of the same page; "Attention mechanism evolution" (toolsku.com) GQA code).
+// block compute the block scores, bring the accumulator and l to a new m when
+// needed, add the block's exp(S - m) V; divide by l at the end.  Causal
+// problems never load key blocks wholly in the future and mask inside the
+// diagonal blocks (§5.5 of the same page).  Query head h reads KV head
+// h / (H / H_kv) (§2 of the same page; "Attention mechanism evolution"
+// (toolsku.com) GQA code).
 //
-// gfx950 mapping (not from the pages; the pages' kernel targets other GPUs):
-//  * workgroup = NW waves, BM = 32*NW query rows; each wave owns 32 rows;
-//  * scores are computed transposed, S^T = K Q^T, with
-//    v_mfma_f32_32x32x16_bf16: A = K fragment from LDS, B = Q fragment held in
-//    VGPRs for the whole kernel.  In the 32x32 accumulator layout lane l holds
-//    column l%32, i.e. one query row, and 16 of the 32 keys, so the row max
-//    and row sum are in-lane plus one exchange with lane l^32;
+// gfx950 mapping (not from the pages, whose kernel targets other GPUs):
+//  * workgroup = NW waves, BM = 32*NW query rows, each wave owns 32 rows; at
+//    NW = 8 two waves share a SIMD, so one wave's softmax overlaps the other's
+//    matrix-core work;
+//  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
+//    (A = K fragment from LDS, B = Q fragment held in VGPRs for the whole
+//    kernel).  In the 32x32 accumulator layout lane l holds column l%32 -- one
+//    query row -- and 16 of the 32 keys, so row max and row sum are in-lane
+//    plus one exchange with lane l^32 (v_permlane32_swap);
 //  * the output is accumulated transposed too, O^T += V^T P^T, so it shares
-//    the one-query-per-lane layout and the rescale by exp(m_old - m_new) is a
-//    per-lane scalar;  P (fp32 -> bf16, round to nearest even) feeds the B
-//    operand straight from the score registers;
-//  * V is stored transposed in LDS (d rows, key columns) with bits 2 and 3 of
-//    the key index swapped inside each 16-key group, which puts the 8 keys a
-//    lane contributes to one MFMA next to each other: one 16-byte LDS read;
-//  * softmax in base 2: scores are scaled by scale*log2(e) once, exp2 is the
-//    hardware v_exp_f32;  lse = ln2 * (m + log2 l) at the end;
-//  * the next K/V tile is fetched into registers while the current one is
-//    being computed; LDS rows are padded so MFMA fragment reads are
-//    bank-conflict free.
+//    the one-row-per-lane layout; P (fp32 -> bf16, round to nearest even) is the
+//    B operand straight from the score registers, and the V^T A operand is read
+//    from the row-major V tile with the transposing LDS read ds_read_b64_tr_b16
+//    (two per MFMA: keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key step, which is
+//    the key order of the score accumulator);
+//  * K and V tiles go from global memory straight into LDS with
+//    buffer_load_dwordx4 ... lds (no VGPR staging); rows past N_k read as 0
+//    through the buffer descriptor's range check and are masked.  Two LDS
+//    buffers: the next tile loads while the current one is used; one barrier
+//    per key block.  16-byte chunks of a row are XOR-swizzled so that both the
+//    K fragment reads and the transposing V reads are bank-conflict free on
+//    the 64-bank LDS;
+//  * softmax in base 2 (scores scaled by scale*log2(e), v_exp_f32); the
+//    running max is only raised -- and O and l rescaled -- when a row's block
+//    maximum exceeds it by more than 8 (so every exp2 argument stays <= 8 and
+//    p <= 256); the result is the same quantity, O = sum p v / sum p, with the
+//    common factor chosen differently; lse = ln2 * (m + log2 l);
+//  * workgroup order: workgroups go to the 8 XCDs round robin; the index is
+//    remapped so each XCD works through a contiguous range of heads (shared
+//    K/V stays in that XCD's L2), longest causal query blocks first within a
+//    group of `group` heads.
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+
+typedef int fa_i32x4 __attribute__((ext_vector_type(4)));
+
+// Global -> LDS direct load: each lane's 16 bytes land at lds + 16 * lane.
+__device__ void fa_raw_buffer_load_lds(fa_i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
+                                       int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
 
 namespace fa {
 namespace {
@@ -41,12 +61,16 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define LDS_AS __attribute__((address_space(3)))
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 struct Params {
     const uint16_t* q;
@@ -57,36 +81,74 @@ struct Params {
     int B, H, H_kv, N_q, N_k;
     int rep;      // H / H_kv
     int nqb;      // query blocks per head
-    float c;      // scale * log2(e)
+    int group;    // heads per longest-first group of the workgroup order
+    float c;      // scale * log2(e), > 0
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Swap bits 2 and 3 of a key index (inside each 16-key group).
-__device__ __forceinline__ int key_swizzle(int key)
+// Buffer descriptor over `bytes` bytes at p (reads past the range return 0).
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, unsigned bytes)
 {
-    int t = ((key >> 2) ^ (key >> 3)) & 1;
-    return key ^ (t * 0xC);
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
+}
+
+// Position of 16-byte chunk c of tile row r inside the row (XOR swizzle).
+template <int D>
+__device__ __forceinline__ int swz(int r, int c)
+{
+    if constexpr (D == 128) return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+    else return c ^ ((r >> 1) & 7);
+}
+
+// Order of workgroups: id -> (query block, head, batch).  Consecutive ids go
+// to different XCDs; the remap gives XCD x the contiguous logical range
+// [x*per, (x+1)*per) when the count divides by 8.
+__device__ __forceinline__ void decompose(int id, int total, const Params& p, bool causal, int& qb, int& h, int& b)
+{
+    int L = id;
+    if ((total & 7) == 0) {
+        const int per = total >> 3;
+        L = (id & 7) * per + (id >> 3);
+    }
+    const int HB = p.H * p.B;
+    // logical order: groups of `group` heads; inside a group, query blocks
+    // longest first (causal), then heads
+    const int gsz = p.group;
+    const int grp = L / (gsz * p.nqb);
+    const int rem = L - grp * gsz * p.nqb;
+    const int h0 = grp * gsz;
+    const int gcount = min(gsz, HB - h0);
+    const int j = rem / gcount;
+    const int bh = h0 + rem % gcount;
+    qb = causal ? p.nqb - 1 - j : j;
+    h = bh % p.H;
+    b = bh / p.H;
 }
 
 template <int D, int NW, int BN, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 {
-    constexpr int BM = NW * 32;          // query rows per workgroup
+    constexpr int BM = NW * 32;              // query rows per workgroup
     constexpr int NTHR = NW * 64;
-    constexpr int KSTEPS = D / 16;       // MFMA k-steps over d for S^T
-    constexpr int DBLK = D / 32;         // 32-row blocks of d for O^T
-    constexpr int NT = BN / 32;          // 32-key sub-tiles per key block
-    constexpr int KROW = D + 8;          // padded K row in LDS (elements)
-    constexpr int VROW = BN + 8;         // padded V^T row in LDS (elements)
-    constexpr int KCH = BN * D / 8;      // 16-byte chunks in a K tile
-    constexpr int KPT = (KCH + NTHR - 1) / NTHR;
-    constexpr int VPAIRS = (BN / 4) * (D / 8);   // (4-key quad, 8-d chunk) pairs
-    constexpr int VPT = (VPAIRS + NTHR - 1) / NTHR;
+    constexpr int KSTEPS = D / 16;           // MFMA k-steps over d for S^T
+    constexpr int DBLK = D / 32;             // 32-row blocks of d for O^T
+    constexpr int NT = BN / 32;              // 32-key sub-tiles per key block
+    constexpr int ROWB = D * 2;              // bytes per K/V row
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int TILE = BN * ROWB;          // bytes per K (or V) tile
+    constexpr int LOADS = TILE / (NTHR * 16);
+    static_assert(TILE % (NTHR * 16) == 0, "tile must be a whole number of wave loads");
     static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KROW];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VROW];
+    // [buffer][K, V][tile]
+    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -94,26 +156,45 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     const int l32 = lane & 31;
     const int half = lane >> 5;
 
-    // ---- work decomposition: one workgroup per (query block, head, batch);
-    //      causal problems run the longest query blocks first
-    const int HB = p.H * p.B;
-    int qb = blockIdx.x / HB;
-    if (CAUSAL) qb = p.nqb - 1 - qb;
-    const int bh = blockIdx.x % HB;
-    const int h = bh % p.H;
-    const int b = bh / p.H;
+    int qb, h, b;
+    decompose(blockIdx.x, gridDim.x, p, CAUSAL, qb, h, b);
     const int g = h / p.rep;
     const int q0 = qb * BM;
-    const int off = p.N_k - p.N_q;                 // causal diagonal offset
-    const int qw0 = q0 + w * 32;                   // first row of this wave
-    const int qi = qw0 + l32;                      // this lane's query row
+    const int off = p.N_k - p.N_q;           // causal diagonal offset
+    const int qw0 = q0 + w * 32;             // first row of this wave
+    const int qi = qw0 + l32;                // this lane's query row
 
     const size_t q_row0 = (size_t)(b * p.H + h) * (size_t)p.N_q;
     const size_t kv_row0 = (size_t)(b * p.H_kv + g) * (size_t)p.N_k;
+    const char* kbase = reinterpret_cast<const char*>(p.k + kv_row0 * D);
+    const char* vbase = reinterpret_cast<const char*>(p.v + kv_row0 * D);
 
     int kend = p.N_k;
     if (CAUSAL) kend = min(p.N_k, q0 + BM + off);
     const int nkb = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+    // ---- per-thread part of a tile load: chunk position -> (row, global chunk)
+    int ld_voff[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int pos = i * NTHR + tid;      // 16-byte chunk position in the tile
+        const int r = pos / CPR, cp = pos % CPR;
+        ld_voff[i] = r * ROWB + swz<D>(r, cp) * 16;
+    }
+    auto issue_tile = [&](int kb, int buf) {
+        const int key0 = kb * BN;
+        const unsigned bytes = (unsigned)min(BN, p.N_k - key0) * ROWB;
+        const i32x4 rk = make_rsrc(kbase + (size_t)key0 * ROWB, bytes);
+        const i32x4 rv = make_rsrc(vbase + (size_t)key0 * ROWB, bytes);
+        char* kt = lds + (buf * 2 + 0) * TILE;
+        char* vt = lds + (buf * 2 + 1) * TILE;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int wpos = (i * NTHR + w * 64) * 16;    // this wave's 1 KB slice
+            fa_raw_buffer_load_lds(rk, (LDS_AS void*)(kt + wpos), 16, ld_voff[i], 0, 0, 0);
+            fa_raw_buffer_load_lds(rv, (LDS_AS void*)(vt + wpos), 16, ld_voff[i], 0, 0, 0);
+        }
+    };
 
     // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole kernel
     bf16x8 qf[KSTEPS];
@@ -122,111 +203,65 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         const u32x4* src = reinterpret_cast<const u32x4*>(p.q + (q_row0 + (size_t)(ok ? qi : 0)) * D);
 #pragma unroll
         for (int ks = 0; ks < KSTEPS; ++ks) {
-            u32x4 t = ok ? src[2 * ks + half] : u32x4{0, 0, 0, 0};
+            const u32x4 t = ok ? src[2 * ks + half] : u32x4{0, 0, 0, 0};
             qf[ks] = __builtin_bit_cast(bf16x8, t);
         }
     }
 
+    // ---- per-lane LDS read offsets
+    // K fragment (A of S^T): row kt*32 + l32, chunk 2*ks + half
+    // V^T fragment (A of O^T) via transposing reads: source row
+    //   kt*32 + s2*16 + 4*half + (lane%16)/4 (+8), column chunk dm*4 + 2*mhi + (lane%4)/2
+    const int j16 = lane & 15;
+    const int mhi = (lane >> 4) & 1;
+    const int vrow_in16 = 4 * half + (j16 >> 2);      // + 8 for the second read
+    const int vsub = (j16 & 1) * 8;                    // byte inside the 16-byte chunk
+
     f32x16 oacc[DBLK];
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
-    float m_run = kNegInf;      // running max, log2 units of the scaled scores
+    float m_run = kNegInf;      // running max (log2 units of the scaled scores)
     float l_run = 0.f;          // this lane's part of the running sum
 
-    // ---- register prefetch of one K/V tile
-    u32x4 kreg[KPT];
-    u32x4 vreg[VPT][4];
-    auto fetch = [&](int kb) {
-        const int key0 = kb * BN;
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * NTHR;
-            const int row = c / (D / 8), col = c % (D / 8);
-            const bool ok = c < KCH && key0 + row < p.N_k;
-            kreg[i] = ok ? reinterpret_cast<const u32x4*>(p.k + (kv_row0 + key0 + row) * D)[col]
-                         : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int c = tid + i * NTHR;
-            const int quad = c % (BN / 4), dch = c / (BN / 4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int key = key0 + quad * 4 + j;
-                const bool ok = c < VPAIRS && key < p.N_k;
-                vreg[i][j] = ok ? reinterpret_cast<const u32x4*>(p.v + (kv_row0 + key) * D)[dch]
-                                : u32x4{0, 0, 0, 0};
-            }
-        }
-    };
-    auto stage = [&]() {
-#pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-            const int c = tid + i * NTHR;
-            if (c < KCH) {
-                const int row = c / (D / 8), col = c % (D / 8);
-                *reinterpret_cast<u32x4*>(&k_lds[row * KROW + col * 8]) = kreg[i];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < VPT; ++i) {
-            const int c = tid + i * NTHR;
-            if (c < VPAIRS) {
-                const int quad = c % (BN / 4), dch = c / (BN / 4);
-                const int kcol = key_swizzle(quad * 4);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    // d = 8*dch + e: gather that element from the four key rows
-                    const int wd = e >> 1;
-                    u32x2 pk;
-                    if (e & 1) {      // odd d: high halves of the four rows
-                        pk[0] = (vreg[i][0][wd] >> 16) | (vreg[i][1][wd] & 0xffff0000u);
-                        pk[1] = (vreg[i][2][wd] >> 16) | (vreg[i][3][wd] & 0xffff0000u);
-                    } else {          // even d: low halves
-                        pk[0] = (vreg[i][0][wd] & 0xffffu) | (vreg[i][1][wd] << 16);
-                        pk[1] = (vreg[i][2][wd] & 0xffffu) | (vreg[i][3][wd] << 16);
-                    }
-                    *reinterpret_cast<u32x2*>(&vt_lds[(dch * 8 + e) * VROW + kcol]) = pk;
-                }
-            }
-        }
-    };
+    if (nkb > 0) issue_tile(0, 0);
 
-    if (nkb > 0) fetch(0);
     for (int kb = 0; kb < nkb; ++kb) {
+        const int buf = kb & 1;
+        // tile kb must be in LDS for every wave; buffer buf^1 must be free
+        __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): this wave's loads landed
         __syncthreads();
-        stage();
-        __syncthreads();
-        if (kb + 1 < nkb) fetch(kb + 1);
+        if (kb + 1 < nkb) issue_tile(kb + 1, buf ^ 1);
 
         const int key0 = kb * BN;
         // wave-level causal skip: the whole block lies after this wave's last row
         if (CAUSAL && key0 > qw0 + 31 + off) continue;
+        const int last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
         const bool need_mask = (key0 + BN > p.N_k) || (CAUSAL && key0 + BN - 1 > qw0 + off);
+
+        const char* kt_lds = lds + (buf * 2 + 0) * TILE;
+        const char* vt_lds = lds + (buf * 2 + 1) * TILE;
 
         // ---- S^T = K Q^T for the BN keys of the block (fp32 accumulate)
         f32x16 s[NT];
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt) {
             s[kt] = f32x16{};
+            const int r = kt * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                    &k_lds[(kt * 32 + l32) * KROW + ks * 16 + half * 8]);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + r * ROWB + swz<D>(r, 2 * ks + half) * 16);
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
             }
         }
 
-        // ---- mask: keys past N_k, and (causal) keys after this row's diagonal
+        // ---- mask keys past this row's last visible key (diagonal / tail blocks)
         if (need_mask) {
+            const int lim = last_vis - key0 - 4 * half;
 #pragma unroll
             for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key0 + kt * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-                    const bool vis = key < p.N_k && (!CAUSAL || key <= qi + off);
-                    if (!vis) s[kt][r] = kNegInf;
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][r] = kNegInf;
         }
 
         // ---- online softmax update of this row
@@ -235,25 +270,31 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mx2 = (mx == kNegInf) ? kNegInf : mx * p.c;
-        const float m_new = fmaxf(m_run, mx2);
-        const float base = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - base);
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+            mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float m_blk = mx * p.c;
+        // raise the running max only when some row's block max exceeds it by > slack
+        if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, m_blk);
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int dm = 0; dm < DBLK; ++dm) oacc[dm] *= alpha;
+            m_run = m_new;
+        }
+        const float base = (m_run == kNegInf) ? 0.f : m_run;
         float lsum = 0.f;
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float e = fast_exp2(__builtin_fmaf(s[kt][r], p.c, -base));
-                if (need_mask && s[kt][r] == kNegInf) e = 0.f;
+                const float e = fast_exp2(__builtin_fmaf(s[kt][r], p.c, -base));
                 s[kt][r] = e;
                 lsum += e;
             }
-        l_run = alpha * l_run + lsum;
-        m_run = m_new;
-#pragma unroll
-        for (int dm = 0; dm < DBLK; ++dm) oacc[dm] *= alpha;
+        l_run += lsum;
 
         // ---- P^T fragments: bf16, 8 keys per MFMA k-step
         bf16x8 pf[NT][2];
@@ -269,19 +310,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 
         // ---- O^T += V^T P^T
 #pragma unroll
-        for (int dm = 0; dm < DBLK; ++dm)
+        for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
-            for (int kt = 0; kt < NT; ++kt)
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int ra = kt * 32 + s2 * 16 + vrow_in16;
+                const int rb = ra + 8;
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-                        &vt_lds[(dm * 32 + l32) * VROW + kt * 32 + s2 * 16 + half * 8]);
+                for (int dm = 0; dm < DBLK; ++dm) {
+                    const int ch = dm * 4 + 2 * mhi + ((j16 >> 1) & 1);
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4*)(vt_lds + ra * ROWB + swz<D>(ra, ch) * 16 + vsub));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (LDS_AS i16x4*)(vt_lds + rb * ROWB + swz<D>(rb, ch) * 16 + vsub));
+                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][s2], oacc[dm], 0, 0, 0);
                 }
+            }
     }
 
     // ---- epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l)
-    const float l_tot = l_run + __shfl_xor(l_run, 32);
+    float l_tot;
+    {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
     if (qi < p.N_q) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         uint16_t* dst = p.o + (q_row0 + qi) * D;
@@ -292,8 +344,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 f32x4 t;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
-                const bf16x4 ob = __builtin_convertvector(t, bf16x4);
-                *reinterpret_cast<bf16x4*>(dst + dm * 32 + gq * 8 + half * 4) = ob;
+                *reinterpret_cast<bf16x4*>(dst + dm * 32 + gq * 8 + half * 4) = __builtin_convertvector(t, bf16x4);
             }
         if (p.lse && half == 0)
             p.lse[q_row0 + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
@@ -301,7 +352,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 }
 
 template <int D, int NW, int BN, bool CAUSAL>
-hipError_t launch(const FwdArgs& a, hipStream_t stream)
+hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
     Params p;
@@ -317,7 +368,10 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream)
     p.N_k = a.N_k;
     p.rep = a.H / a.H_kv;
     p.nqb = (a.N_q + BM - 1) / BM;
-    p.c = a.scale * kLog2e;
+    p.group = group < 1 ? 1 : group;
+    // scale 0 runs as a tiny positive scale: every exp2 argument then rounds to
+    // 0 exactly as with scale 0, and masked scores stay -inf instead of NaN
+    p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
     const long long blocks = (long long)p.nqb * a.H * a.B;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
@@ -326,12 +380,17 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream)
 
 }  // namespace
 
+#ifndef FA_FWD_GROUP
+#define FA_FWD_GROUP 4
+#endif
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream)
 {
+    const int group = FA_FWD_GROUP;
     if (a.d == 128)
-        return a.causal ? launch<128, 4, 64, true>(a, stream) : launch<128, 4, 64, false>(a, stream);
+        return a.causal ? launch<128, 8, 64, true>(a, group, stream) : launch<128, 8, 64, false>(a, group, stream);
     if (a.d == 64)
-        return a.causal ? launch<64, 4, 64, true>(a, stream) : launch<64, 4, 64, false>(a, stream);
+        return a.causal ? launch<64, 8, 64, true>(a, group, stream) : launch<64, 8, 64, false>(a, group, stream);
     return hipErrorInvalidValue;
 }
 
