@@ -45,6 +45,7 @@
 
 #include <hip/hip_runtime.h>
 #include <cstdint>
+#include <type_traits>
 
 typedef int fa_i32x4 __attribute__((ext_vector_type(4)));
 
@@ -66,6 +67,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 #define LDS_AS __attribute__((address_space(3)))
+
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -107,45 +109,47 @@ __device__ __forceinline__ int swz(int r, int c)
     else return c ^ ((r >> 1) & 7);
 }
 
-// Order of workgroups: id -> (query block, head, batch).  Consecutive ids go
-// to different XCDs; the remap gives XCD x the contiguous logical range
-// [x*per, (x+1)*per) when the count divides by 8.
-__device__ __forceinline__ void decompose(int id, int total, const Params& p, bool causal, int& qb, int& h, int& b)
+// Order of workgroups: id -> (query block, head, batch).  Workgroups are
+// dispatched to the 8 XCDs round robin (id % 8).  When the head count divides
+// by 8, XCD x owns the contiguous heads [x*HB/8, (x+1)*HB/8) -- heads that
+// share a KV head land on the same XCD and its L2 -- and walks them in groups
+// of `group` heads, longest causal query blocks first inside a group.
+__device__ __forceinline__ void decompose(int id, const Params& p, bool causal, int& qb, int& h, int& b)
 {
-    int L = id;
-    if ((total & 7) == 0) {
-        const int per = total >> 3;
-        L = (id & 7) * per + (id >> 3);
-    }
     const int HB = p.H * p.B;
-    // logical order: groups of `group` heads; inside a group, query blocks
-    // longest first (causal), then heads
-    const int gsz = p.group;
-    const int grp = L / (gsz * p.nqb);
-    const int rem = L - grp * gsz * p.nqb;
-    const int h0 = grp * gsz;
-    const int gcount = min(gsz, HB - h0);
+    int head0 = 0, nheads = HB, slot = id;
+    if ((HB & 7) == 0) {
+        nheads = HB >> 3;
+        head0 = (id & 7) * nheads;
+        slot = id >> 3;
+    }
+    const int gsz = min(p.group, nheads);
+    const int grp = slot / (gsz * p.nqb);
+    const int rem = slot - grp * gsz * p.nqb;
+    const int g0 = grp * gsz;
+    const int gcount = min(gsz, nheads - g0);
     const int j = rem / gcount;
-    const int bh = h0 + rem % gcount;
+    const int bh = head0 + g0 + rem % gcount;
     qb = causal ? p.nqb - 1 - j : j;
     h = bh % p.H;
     b = bh / p.H;
 }
 
-template <int D, int NW, int BN, bool CAUSAL>
+template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 {
     constexpr int BM = NW * 32;              // query rows per workgroup
     constexpr int NTHR = NW * 64;
+    constexpr int BN = 64;                   // keys per LDS tile
     constexpr int KSTEPS = D / 16;           // MFMA k-steps over d for S^T
     constexpr int DBLK = D / 32;             // 32-row blocks of d for O^T
-    constexpr int NT = BN / 32;              // 32-key sub-tiles per key block
+    constexpr int NT = BN / 32;              // 32-key sub-tiles per tile
     constexpr int ROWB = D * 2;              // bytes per K/V row
     constexpr int CPR = D / 8;               // 16-byte chunks per row
     constexpr int TILE = BN * ROWB;          // bytes per K (or V) tile
     constexpr int LOADS = TILE / (NTHR * 16);
     static_assert(TILE % (NTHR * 16) == 0, "tile must be a whole number of wave loads");
-    static_assert(BN % 32 == 0 && D % 32 == 0, "tile shape");
+    static_assert(D % 32 == 0, "tile shape");
 
     // [buffer][K, V][tile]
     __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE];
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     const int half = lane >> 5;
 
     int qb, h, b;
-    decompose(blockIdx.x, gridDim.x, p, CAUSAL, qb, h, b);
+    decompose(blockIdx.x, p, CAUSAL, qb, h, b);
     const int g = h / p.rep;
     const int q0 = qb * BM;
     const int off = p.N_k - p.N_q;           // causal diagonal offset
@@ -172,8 +176,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     int kend = p.N_k;
     if (CAUSAL) kend = min(p.N_k, q0 + BM + off);
     const int nkb = kend > 0 ? (kend + BN - 1) / BN : 0;
+    const int last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
 
-    // ---- per-thread part of a tile load: chunk position -> (row, global chunk)
+    // ---- tile loads: chunk position -> (row, global chunk)
     int ld_voff[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
@@ -208,53 +213,64 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         }
     }
 
-    // ---- per-lane LDS read offsets
-    // K fragment (A of S^T): row kt*32 + l32, chunk 2*ks + half
-    // V^T fragment (A of O^T) via transposing reads: source row
-    //   kt*32 + s2*16 + 4*half + (lane%16)/4 (+8), column chunk dm*4 + 2*mhi + (lane%4)/2
-    const int j16 = lane & 15;
-    const int mhi = (lane >> 4) & 1;
-    const int vrow_in16 = 4 * half + (j16 >> 2);      // + 8 for the second read
-    const int vsub = (j16 & 1) * 8;                    // byte inside the 16-byte chunk
+    // ---- per-lane LDS read offsets inside a tile, computed once.  The
+    //      swizzle only depends on the row modulo 16, so moving by 16 or 32 rows
+    //      is a constant added to these (an instruction immediate).
+    // K fragment (A of S^T): row l32, chunk 2*ks + half
+    int k_off[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) k_off[ks] = l32 * ROWB + swz<D>(l32, 2 * ks + half) * 16;
+    // V^T fragment (A of O^T) through transposing reads: source row
+    // 4*half + (lane%16)/4 (+8 for keys 8..15 of the 16-key step), column
+    // chunk 4*dm + 2*((lane/16)%2) + (lane/2)%2, 8-byte half (lane%2)
+    int v_off[2][DBLK];
+    {
+        const int j16 = lane & 15;
+        const int vra = 4 * half + (j16 >> 2);
+        const int vch = 2 * ((lane >> 4) & 1) + ((j16 >> 1) & 1);
+#pragma unroll
+        for (int ab = 0; ab < 2; ++ab)
+#pragma unroll
+            for (int dm = 0; dm < DBLK; ++dm) {
+                const int r = vra + 8 * ab;
+                v_off[ab][dm] = r * ROWB + swz<D>(r, dm * 4 + vch) * 16 + (j16 & 1) * 8;
+            }
+    }
 
     f32x16 oacc[DBLK];
 #pragma unroll
     for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
     float m_run = kNegInf;      // running max (log2 units of the scaled scores)
-    float l_run = 0.f;          // this lane's part of the running sum
+    float nbase = 0.f;          // -m_run, or 0 while the row has seen no key
+    float l_a = 0.f, l_b = 0.f; // this lane's part of the running sum (two chains)
 
-    if (nkb > 0) issue_tile(0, 0);
-
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        // tile kb must be in LDS for every wave; buffer buf^1 must be free
+    auto body = [&](int kb, auto bufc) {
+        constexpr int BUF = decltype(bufc)::value;
+        const char* kt_lds = lds + (BUF * 2 + 0) * TILE;
+        const char* vt_lds = lds + (BUF * 2 + 1) * TILE;
+        // tile kb must be in LDS for every wave; the other buffer must be free
         __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): this wave's loads landed
         __syncthreads();
-        if (kb + 1 < nkb) issue_tile(kb + 1, buf ^ 1);
+        if (kb + 1 < nkb) issue_tile(kb + 1, BUF ^ 1);
 
         const int key0 = kb * BN;
-        // wave-level causal skip: the whole block lies after this wave's last row
-        if (CAUSAL && key0 > qw0 + 31 + off) continue;
-        const int last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
+        // wave-level causal skip: the whole tile lies after this wave's last row
+        if (CAUSAL && key0 > qw0 + 31 + off) return;
         const bool need_mask = (key0 + BN > p.N_k) || (CAUSAL && key0 + BN - 1 > qw0 + off);
 
-        const char* kt_lds = lds + (buf * 2 + 0) * TILE;
-        const char* vt_lds = lds + (buf * 2 + 1) * TILE;
-
-        // ---- S^T = K Q^T for the BN keys of the block (fp32 accumulate)
+        // ---- S^T = K Q^T for the BN keys of the tile (fp32 accumulate)
         f32x16 s[NT];
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt) {
             s[kt] = f32x16{};
-            const int r = kt * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + r * ROWB + swz<D>(r, 2 * ks + half) * 16);
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + kt * 32 * ROWB + k_off[ks]);
                 s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
             }
         }
 
-        // ---- mask keys past this row's last visible key (diagonal / tail blocks)
+        // ---- mask keys past this row's last visible key (diagonal / tail tiles)
         if (need_mask) {
             const int lim = last_vis - key0 - 4 * half;
 #pragma unroll
@@ -264,7 +280,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                     if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][r] = kNegInf;
         }
 
-        // ---- online softmax update of this row
+        // ---- online softmax: row max of the tile, raise the running max only
+        //      when it grows by more than the slack (then rescale O and l)
         float mx = kNegInf;
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt)
@@ -275,28 +292,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
         }
         const float m_blk = mx * p.c;
-        // raise the running max only when some row's block max exceeds it by > slack
         if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kRescaleSlack)) {
             const float m_new = fmaxf(m_run, m_blk);
             const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
-            l_run *= alpha;
+            l_a *= alpha;
+            l_b *= alpha;
 #pragma unroll
             for (int dm = 0; dm < DBLK; ++dm) oacc[dm] *= alpha;
             m_run = m_new;
+            nbase = (m_new == kNegInf) ? 0.f : -m_new;
         }
-        const float base = (m_run == kNegInf) ? 0.f : m_run;
-        float lsum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < NT; ++kt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float e = fast_exp2(__builtin_fmaf(s[kt][r], p.c, -base));
-                s[kt][r] = e;
-                lsum += e;
-            }
-        l_run += lsum;
 
-        // ---- P^T fragments: bf16, 8 keys per MFMA k-step
+        // ---- P = exp2(c*s - m): summed in fp32 (the lse needs the unrounded
+        //      weights), rounded to bf16 as the B operand of O^T += V^T P^T
         bf16x8 pf[NT][2];
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt)
@@ -304,7 +312,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             for (int s2 = 0; s2 < 2; ++s2) {
                 f32x8 t;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) t[i] = s[kt][s2 * 8 + i];
+                for (int i = 0; i < 8; ++i) t[i] = fast_exp2(__builtin_fmaf(s[kt][s2 * 8 + i], p.c, nbase));
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    l_a += t[i];
+                    l_b += t[i + 1];
+                }
                 pf[kt][s2] = __builtin_convertvector(t, bf16x8);
             }
 
@@ -313,24 +326,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
-                const int ra = kt * 32 + s2 * 16 + vrow_in16;
-                const int rb = ra + 8;
+                const char* vp = vt_lds + (kt * 32 + s2 * 16) * ROWB;
 #pragma unroll
                 for (int dm = 0; dm < DBLK; ++dm) {
-                    const int ch = dm * 4 + 2 * mhi + ((j16 >> 1) & 1);
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS i16x4*)(vt_lds + ra * ROWB + swz<D>(ra, ch) * 16 + vsub));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                        (LDS_AS i16x4*)(vt_lds + rb * ROWB + swz<D>(rb, ch) * 16 + vsub));
+                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[0][dm]));
+                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[1][dm]));
                     const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
                     oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][s2], oacc[dm], 0, 0, 0);
                 }
             }
+    };
+
+    if (nkb > 0) issue_tile(0, 0);
+    for (int kb = 0; kb < nkb; kb += 2) {
+        body(kb, std::integral_constant<int, 0>{});
+        if (kb + 1 < nkb) body(kb + 1, std::integral_constant<int, 1>{});
     }
 
     // ---- epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l)
     float l_tot;
     {
+        const float l_run = l_a + l_b;
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
@@ -351,7 +367,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     }
 }
 
-template <int D, int NW, int BN, bool CAUSAL>
+template <int D, int NW, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
@@ -374,23 +390,23 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
     const long long blocks = (long long)p.nqb * a.H * a.B;
     if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, BN, CAUSAL>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
 }  // namespace
 
 #ifndef FA_FWD_GROUP
-#define FA_FWD_GROUP 4
+#define FA_FWD_GROUP 8
 #endif
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream)
 {
     const int group = FA_FWD_GROUP;
     if (a.d == 128)
-        return a.causal ? launch<128, 8, 64, true>(a, group, stream) : launch<128, 8, 64, false>(a, group, stream);
+        return a.causal ? launch<128, 8, true>(a, group, stream) : launch<128, 8, false>(a, group, stream);
     if (a.d == 64)
-        return a.causal ? launch<64, 8, 64, true>(a, group, stream) : launch<64, 8, 64, false>(a, group, stream);
+        return a.causal ? launch<64, 8, true>(a, group, stream) : launch<64, 8, false>(a, group, stream);
     return hipErrorInvalidValue;
 }
 
