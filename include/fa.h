@@ -113,8 +113,11 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *   q         [B,H,d]          bf16, device
  *   k_cache   [B,H_kv,N_max,d] bf16, device; rows >= seq_lens[b] are never read
  *   v_cache   [B,H_kv,N_max,d] bf16, device; same
- *   seq_lens  [B] int32, device; each value must lie in 1..N_max (trusted:
- *             the library does not read device memory on the host)
+ *   seq_lens  [B] int32, device; each value should lie in 0..N_max.  The
+ *             library does not read device memory on the host, so it cannot
+ *             report a bad value; the kernels clamp each one into 0..N_max,
+ *             so the cache is never read outside its rows.  A length of 0
+ *             gives o = 0 and lse = -inf for that sequence.
  *   o         [B,H,d] bf16, device, written
  *   lse       [B,H]   fp32, device, written; may be NULL
  *   B, H, H_kv, N_max >= 1; H % H_kv == 0; d in {64, 128}

@@ -218,13 +218,33 @@ def test_decode_split_counts_and_edge_lengths(num_splits):
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"S={num_splits}")
 
 
-@pytest.mark.parametrize("H,H_kv,d", [(16, 1, 64), (12, 4, 128), (8, 8, 128), (64, 8, 128)])
+@pytest.mark.parametrize("H,H_kv,d", [(16, 1, 64), (12, 4, 128), (8, 8, 128), (64, 8, 128),
+                                      (40, 2, 128), (48, 1, 64), (64, 2, 128)])
 def test_decode_head_sharing(H, H_kv, d):
     spec = _small_decode_spec(H=H, H_kv=H_kv, d=d, N_max=1200, B=3, seed=13)
     data = inputs.decode_inputs(spec)
     o, lse = _decode_run(data, 8)
     o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale)
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+def test_decode_lengths_outside_the_cache_are_clamped():
+    """A length <= 0 gives the empty result (o = 0, lse = -inf); one past N_max
+    attends to the whole cache and reads nothing beyond it."""
+    import torch
+    spec = _small_decode_spec(H=8, H_kv=2, d=128, N_max=700, B=6, seed=19)
+    dev_lens = np.array([0, 5, 700 + 333, -3, 1, 700], np.int32)
+    host_lens = np.array([1, 5, 700, 1, 1, 700], np.int32)   # clamped; rows 0 and 3 are replaced below
+    data = inputs.decode_inputs(spec, seq_lens=host_lens)
+    q = bf16_to_device(data.q)
+    kc, vc = bf16_to_device(data.k_cache), bf16_to_device(data.v_cache)
+    o, lse = api.decode(q, kc, vc, torch.from_numpy(dev_lens).cuda(), num_splits=8, scale=spec.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, host_lens, spec.scale)
+    for b in (0, 3):
+        o_ref[b] = 0.0
+        lse_ref[b] = -np.inf
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label="clamped lengths")
 
 
 def test_decode_deterministic():

@@ -35,9 +35,16 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# per-source extras: the decode kernel rescales its accumulators in place, so
+# its matrix-core products accumulate in ordinary VGPRs rather than AGPRs
+# (which would need copies in and out on every rescale)
+EXTRA_FLAGS = {
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
 
 def _compile(src: str, obj: str) -> None:
-    cmd = [HIPCC, *COMMON_FLAGS]
+    cmd = [HIPCC, *COMMON_FLAGS, *EXTRA_FLAGS.get(src, [])]
     if src.endswith(".cpp"):
         cmd += ["-x", "hip"]
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]

@@ -9,15 +9,25 @@
 // cache, so it is bound by memory bandwidth, and §2: a KV head serves
 // H/H_kv query heads).
 //
-// Split pass: workgroup (c, head group, b) takes keys
-// [c*L, min((c+1)*L, len)) with L = ceil(len / num_splits) and serves HG query
-// heads that share one KV head, so each K/V byte of the chunk is read from HBM
-// once for all of them.  Rows are streamed with 16-byte loads, D/8 lanes per
-// row, several rows in flight per lane.  Each row slot of a wave keeps its own
-// running max / running sum / output (the online softmax of "Attention
-// variants" §3); row slots and waves are merged at the end with the same
-// rescale rule.  The chunk result is written as o_c = O/l (fp32) and
-// lse_c = m + ln l; an empty chunk writes lse_c = -inf, o_c = 0.
+// Split pass: workgroup (c, KV head and head group, b) takes keys
+// [c*L, min((c+1)*L, len)) with L = ceil(len / num_splits) and serves up to 16
+// query heads that share one KV head, so each K/V byte of the chunk crosses HBM
+// once for all of them.  The chunk is cut into 16-key tiles dealt round robin
+// to the 4 waves; each wave streams its tiles into its own slice of LDS with
+// buffer_load_dwordx4 ... lds (two tiles in flight, no workgroup barrier) and
+// computes on the matrix cores:
+//   S^T (16 keys x 16 heads) = K Q^T     v_mfma_f32_16x16x32_bf16, K from LDS
+//   O^T (d x 16 heads)     += V^T P^T    v_mfma_f32_16x16x16_bf16, V^T from LDS
+//                                         through transposing reads
+// In the 16x16 accumulator layout lane l holds head l%16 and keys 4*(l/16)..+3
+// of the tile, which is exactly the B operand the 16x16x16 P V product needs,
+// so P goes from the score registers to the matrix core with one conversion.
+// Padding heads (past the group) have zero queries and are discarded.  The
+// online softmax of "Attention variants" §3 runs per wave (running max raised
+// only when a tile max exceeds it by more than 8, so p <= 256); the 4 waves
+// are merged at the end with the same rescale rule and the chunk writes
+// o_c = O/l (fp32) and lse_c = m + ln l; an empty chunk writes lse_c = -inf,
+// o_c = 0.
 //
 // Merge pass (not on the pages; the online-softmax rescale applied to whole
 // chunk summaries): M = max_c lse_c, lse = M + ln sum_c exp(lse_c - M),
@@ -27,17 +37,31 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+typedef int fa_dec_i32x4 __attribute__((ext_vector_type(4)));
+
+// Global -> LDS direct load: each lane's 16 bytes land at lds + 16 * lane.
+__device__ void fa_dec_buffer_load_lds(fa_dec_i32x4 rsrc, __attribute__((address_space(3))) void* lds, int size,
+                                       int voffset, int soffset, int offset, int aux)
+    __asm("llvm.amdgcn.raw.buffer.load.lds");
+
 namespace fa {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#define LDS_AS __attribute__((address_space(3)))
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
+constexpr float kRescaleSlack = 8.0f;   // log2 units
 
 struct SplitParams {
     const uint16_t* q;
@@ -46,191 +70,281 @@ struct SplitParams {
     const int* seq_lens;
     float* part_o;
     float* part_lse;
-    int H, H_kv, N_max, S, rep;
-    float c;      // scale * log2(e)
+    int H, H_kv, N_max, S, rep, ngrp;
+    float c;      // scale * log2(e), > 0
 };
 
-__device__ __forceinline__ float bf_lo(unsigned w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf_hi(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Sum over the LPR consecutive lanes that hold one cache row (DPP within a row of 16).
-template <int LPR>
-__device__ __forceinline__ float row_sum(float x)
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, unsigned bytes)
 {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));  // lane ^ 1
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));  // lane ^ 2
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x141, 0xF, 0xF, false)); // mirror in 8
-    if (LPR == 16)
-        x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x140, 0xF, 0xF, false)); // mirror in 16
-    return x;
+    const uint64_t a = reinterpret_cast<uint64_t>(p);
+    i32x4 r;
+    r[0] = __builtin_amdgcn_readfirstlane((int)(a & 0xffffffffu));
+    r[1] = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));
+    r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+    r[3] = 0x00020000;
+    return r;
 }
 
-// Merge running state (m, l, o) with another one (all in log2 units).
+// Position of 16-byte chunk c of row r (0..15) of a 16-key tile.  Conflict
+// free for the K fragment reads (16 rows, one chunk) and for the transposing
+// V reads (8 rows, two adjacent chunks) on the 64-bank LDS.
+template <int D>
+__device__ __forceinline__ int dswz(int r, int c)
+{
+    if constexpr (D == 128) return c ^ (2 * (r & 7) + ((r >> 3) & 1));
+    else return c ^ (2 * ((r >> 1) & 3) + ((r >> 3) & 1));
+}
+
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
 template <int N>
-__device__ __forceinline__ void merge_state(float& m, float& l, float* o, float m2, float l2, const float* o2)
+__device__ __forceinline__ void wait_vmcnt()
 {
-    const float mn = fmaxf(m, m2);
-    const float base = (mn == kNegInf) ? 0.f : mn;
-    const float a1 = fast_exp2(m - base), a2 = fast_exp2(m2 - base);
-    l = a1 * l + a2 * l2;
-#pragma unroll
-    for (int i = 0; i < N; ++i) o[i] = a1 * o[i] + a2 * o2[i];
-    m = mn;
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int D, int HG>
+__device__ __forceinline__ float swap32_max(float x)
+{
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float swap16_max(float x)
+{
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float swap32_sum(float x)
+{
+    const auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+__device__ __forceinline__ float swap16_sum(float x)
+{
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// LDS reads of one tile.  They are written as asm blocks that wait for their
+// own results: the compiler treats any LDS read that follows a global->LDS
+// load as possibly reading its destination and would wait for every load in
+// flight, which would serialise the two-stage pipeline; the stage discipline
+// (explicit vmcnt waits below) is what orders these reads after their tile.
+__device__ __forceinline__ void lds_read_k4(bf16x8 (&a)[4], unsigned p0, unsigned p1, unsigned p2, unsigned p3)
+{
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+                 : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+                 : "memory");
+}
+__device__ __forceinline__ void lds_read_k2(bf16x8 (&a)[2], unsigned p0, unsigned p1)
+{
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1])
+                 : "v"(p0), "v"(p1)
+                 : "memory");
+}
+// transposing 4x16-bit reads: result lane i of each 16-lane group holds
+// column i of the 4 rows addressed by lanes i/4, i/4+4, i/4+8, i/4+12
+__device__ __forceinline__ void lds_read_vt8(i16x4 (&a)[8], const unsigned (&p)[8])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %8\n\tds_read_b64_tr_b16 %1, %9\n\t"
+                 "ds_read_b64_tr_b16 %2, %10\n\tds_read_b64_tr_b16 %3, %11\n\t"
+                 "ds_read_b64_tr_b16 %4, %12\n\tds_read_b64_tr_b16 %5, %13\n\t"
+                 "ds_read_b64_tr_b16 %6, %14\n\tds_read_b64_tr_b16 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]),
+                   "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]), "=&v"(a[7])
+                 : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+                 : "memory");
+}
+__device__ __forceinline__ void lds_read_vt4(i16x4 (&a)[4], const unsigned (&p)[4])
+{
+    asm volatile("ds_read_b64_tr_b16 %0, %4\n\tds_read_b64_tr_b16 %1, %5\n\t"
+                 "ds_read_b64_tr_b16 %2, %6\n\tds_read_b64_tr_b16 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+                 : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+                 : "memory");
+}
+
+template <int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
 {
     constexpr int NW = 4;
-    constexpr int LPR = D / 8;           // lanes per cache row
-    constexpr int RPW = 64 / LPR;        // rows per wave per load
-    constexpr int U = 4;                 // loads in flight per lane (per K and per V)
-    constexpr int ROWS_WAVE = RPW * U;   // rows per wave per iteration
-    constexpr int ROWS_ITER = NW * ROWS_WAVE;
+    constexpr int TK = 16;                   // keys per tile
+    constexpr int ROWB = D * 2;
+    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int TILEB = TK * ROWB;         // bytes per K (or V) tile
+    constexpr int LOADS = TILEB / (64 * 16); // wave load instructions per tensor per tile
+    constexpr int KS = D / 32;               // 16x16x32 k-steps over d
+    constexpr int DB = D / 16;               // 16-row blocks of d for O^T
+    constexpr int WAVE_LDS = 2 * 2 * TILEB;  // two stages of (K, V) per wave
+    static_assert(TILEB % (64 * 16) == 0, "tile shape");
 
-    __shared__ float sh_m[NW][HG];
-    __shared__ float sh_l[NW][HG];
-    __shared__ float sh_o[NW][HG][D];
+    constexpr int QB = 16 * 256;             // Q rows of the head group (16 x 256 B at most)
+    __shared__ __attribute__((aligned(1024))) char lds[NW * WAVE_LDS + QB];
 
     const int c = blockIdx.x;
-    const int h0 = blockIdx.y * HG;
+    const int g = blockIdx.y / p.ngrp;
+    const int hg = blockIdx.y % p.ngrp;
     const int b = blockIdx.z;
-    const int g = h0 / p.rep;
+    const int h0 = g * p.rep + hg * 16;      // first query head of the group
+    const int nh = min(16, p.rep - hg * 16); // heads in the group
     const int tid = threadIdx.x;
-    const int w = tid >> 6, lane = tid & 63;
-    const int slot = lane / LPR;         // which row of a load this lane serves
-    const int dl = lane % LPR;           // 8 elements d = 8*dl .. 8*dl+7
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int l16 = lane & 15, g4 = lane >> 4;
 
-    const int len = p.seq_lens[b];
+    const int len = min(max(p.seq_lens[b], 0), p.N_max);   // never outside the cache
     const int L = (len + p.S - 1) / p.S;
     const int j0 = c * L;
-    const int j1 = min(j0 + L, len);
+    const int nkeys = max(0, min(j0 + L, len) - j0);
+    const int ntiles = (nkeys + TK - 1) / TK;
+    const int nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles w, w+4, ...
 
-    // queries of the HG heads, pre-scaled by scale*log2(e): scores come out in log2 units
-    float q[HG][8];
+    const size_t kv_row0 = ((size_t)b * p.H_kv + g) * (size_t)p.N_max + (size_t)j0;
+    const char* kbase = reinterpret_cast<const char*>(p.k + kv_row0 * D);
+    const char* vbase = reinterpret_cast<const char*>(p.v + kv_row0 * D);
+    char* wl = lds + w * WAVE_LDS;
+
+    int ld_off[LOADS];
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-        const u32x4 t = reinterpret_cast<const u32x4*>(p.q + ((size_t)b * p.H + h0 + hh) * D)[dl];
+    for (int i = 0; i < LOADS; ++i) {
+        const int pos = i * 64 + lane;
+        const int r = pos / CPR, cp = pos % CPR;
+        ld_off[i] = r * ROWB + dswz<D>(r, cp) * 16;
+    }
+    // tile t of the chunk into stage s: rows past the chunk read as 0
+    auto issue = [&](int t, int s) __attribute__((always_inline)) {
+        const int key0 = t * TK;
+        const unsigned bytes = (unsigned)min(TK, nkeys - key0) * ROWB;
+        const i32x4 rk = make_rsrc(kbase + (size_t)key0 * ROWB, bytes);
+        const i32x4 rv = make_rsrc(vbase + (size_t)key0 * ROWB, bytes);
+        char* dst = wl + s * 2 * TILEB;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            q[hh][2 * i] = bf_lo(t[i]) * p.c;
-            q[hh][2 * i + 1] = bf_hi(t[i]) * p.c;
+        for (int i = 0; i < LOADS; ++i) {
+            fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_off[i], 0, 0, 0);
+            fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_off[i], 0, 0, 0);
         }
+    };
+
+    // per-lane LDS read offsets inside a stage
+    int k_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) k_off[ks] = l16 * ROWB + dswz<D>(l16, 4 * ks + g4) * 16;
+    int v_off[DB];
+    {
+        const int r = 4 * g4 + (l16 >> 2);
+#pragma unroll
+        for (int dm = 0; dm < DB; ++dm)
+            v_off[dm] = TILEB + r * ROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 + (l16 & 1) * 8;
     }
 
-    float m[HG], l[HG], o[HG][8];
+    f32x4 oacc[DB];
 #pragma unroll
-    for (int hh = 0; hh < HG; ++hh) {
-        m[hh] = kNegInf;
-        l[hh] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[hh][i] = 0.f;
+    for (int i = 0; i < DB; ++i) oacc[i] = f32x4{};
+    float m_run = kNegInf, nbase = 0.f, l_run = 0.f;
+
+    // ---- Q rows of the group into LDS (one 1 KB slice per wave; rows past the
+    // group read as 0), then the first two tiles of this wave
+    char* qs = lds + NW * WAVE_LDS;
+    {
+        const i32x4 rq = make_rsrc(p.q + ((size_t)b * p.H + h0) * D, (unsigned)nh * ROWB);
+        fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, w * 1024 + lane * 16, 0, 0, 0);
+    }
+    if (nt_w > 0) issue(w, 0);
+    if (nt_w > 1) issue(w + NW, 1);
+    if (nt_w > 1) wait_vmcnt<4 * LOADS>();      // the Q slice (older than both tiles) landed
+    else if (nt_w > 0) wait_vmcnt<2 * LOADS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();               // every wave waited for its own slice
+    // Q^T fragments (B of S^T): head l16, d = 32*ks + 8*g4 .. +8
+    bf16x8 qf[KS];
+    {
+        const unsigned qa = (unsigned)(uintptr_t)(LDS_AS char*)qs + l16 * ROWB + g4 * 16;
+        if constexpr (KS == 4) lds_read_k4(qf, qa, qa + 64, qa + 128, qa + 192);
+        else lds_read_k2(qf, qa, qa + 64);
     }
 
-    const size_t kv_row0 = ((size_t)b * p.H_kv + g) * (size_t)p.N_max;
-    const u32x4* kbase = reinterpret_cast<const u32x4*>(p.k + kv_row0 * D) + dl;
-    const u32x4* vbase = reinterpret_cast<const u32x4*>(p.v + kv_row0 * D) + dl;
+    const unsigned wl_addr = (unsigned)(uintptr_t)(LDS_AS char*)wl;
+    auto compute = [&](int t, int s) __attribute__((always_inline)) {
+        const unsigned st = wl_addr + s * 2 * TILEB;
+        bf16x8 kf[KS];
+        if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
+        else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
+        f32x4 sc = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
+        unsigned vaddr[DB];
+#pragma unroll
+        for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
+        i16x4 vf[DB];
+        if constexpr (DB == 8) lds_read_vt8(vf, vaddr);
+        else lds_read_vt4(vf, vaddr);
+        // keys past the chunk end
+        const int lim = nkeys - t * TK - 4 * g4;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[r] = (r < lim) ? sc[r] : kNegInf;
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        mx = swap16_max(swap32_max(mx));
+        const float m_blk = mx * p.c;
+        if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kRescaleSlack)) {
+            const float m_new = fmaxf(m_run, m_blk);
+            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
+            l_run *= alpha;
+#pragma unroll
+            for (int dm = 0; dm < DB; ++dm) oacc[dm] *= alpha;
+            m_run = m_new;
+            nbase = (m_new == kNegInf) ? 0.f : -m_new;
+        }
+        f32x4 e;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
+        l_run += (e[0] + e[1]) + (e[2] + e[3]);
+        const bf16x4 pf = __builtin_convertvector(e, bf16x4);
+#pragma unroll
+        for (int dm = 0; dm < DB; ++dm)
+            oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vf[dm]), pf, oacc[dm], 0, 0, 0);
+    };
 
-    for (int r0 = j0; r0 < j1; r0 += ROWS_ITER) {
-        u32x4 kr[U], vr[U];
-        bool ok[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = r0 + w * ROWS_WAVE + u * RPW + slot;
-            ok[u] = j < j1;
-            kr[u] = ok[u] ? kbase[(size_t)j * (D / 8)] : u32x4{0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int j = r0 + w * ROWS_WAVE + u * RPW + slot;
-            vr[u] = ok[u] ? vbase[(size_t)j * (D / 8)] : u32x4{0, 0, 0, 0};
-        }
-        // scores of the U rows for the HG heads
-        float s[U][HG];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float kf[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kf[2 * i] = bf_lo(kr[u][i]);
-                kf[2 * i + 1] = bf_hi(kr[u][i]);
-            }
-#pragma unroll
-            for (int hh = 0; hh < HG; ++hh) {
-                float acc = 0.f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(q[hh][i], kf[i], acc);
-                s[u][hh] = row_sum<LPR>(acc);
-            }
-        }
-        // online softmax over the U rows of this slot
-        float vf[U][8];
-#pragma unroll
-        for (int u = 0; u < U; ++u)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                vf[u][2 * i] = bf_lo(vr[u][i]);
-                vf[u][2 * i + 1] = bf_hi(vr[u][i]);
-            }
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-            float mx = kNegInf;
-#pragma unroll
-            for (int u = 0; u < U; ++u) mx = fmaxf(mx, ok[u] ? s[u][hh] : kNegInf);
-            const float mn = fmaxf(m[hh], mx);
-            const float base = (mn == kNegInf) ? 0.f : mn;
-            const float alpha = fast_exp2(m[hh] - base);
-            float pr[U];
-            float ps = 0.f;
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                pr[u] = ok[u] ? fast_exp2(s[u][hh] - base) : 0.f;
-                ps += pr[u];
-            }
-            l[hh] = alpha * l[hh] + ps;
-            m[hh] = mn;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float acc = o[hh][i] * alpha;
-#pragma unroll
-                for (int u = 0; u < U; ++u) acc = __builtin_fmaf(pr[u], vf[u][i], acc);
-                o[hh][i] = acc;
-            }
-        }
+    // ---- stream this wave's tiles: two in flight, no workgroup barrier
+    for (int i = 0; i < nt_w; ++i) {
+        if (i + 1 < nt_w) wait_vmcnt<2 * LOADS>();     // tile i landed, tile i+1 may still fly
+        else wait_vmcnt<0>();
+        compute(w + i * NW, i & 1);
+        if (i + 2 < nt_w) issue(w + (i + 2) * NW, i & 1);   // this stage's reads are complete
     }
 
-    // merge the row slots of this wave (lanes with equal dl)
-#pragma unroll
-    for (int x = LPR; x < 64; x <<= 1) {
-#pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-            const float m2 = __shfl_xor(m[hh], x);
-            const float l2 = __shfl_xor(l[hh], x);
-            float o2[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) o2[i] = __shfl_xor(o[hh][i], x);
-            merge_state<8>(m[hh], l[hh], o[hh], m2, l2, o2);
-        }
+    // ---- merge the 4 waves through LDS and write the chunk's partial result
+    const float l_head = swap16_sum(swap32_sum(l_run));      // sum over the 4 key groups
+    __syncthreads();                                          // tile slices are free
+    float* sh_m = reinterpret_cast<float*>(lds);             // [NW][16]
+    float* sh_l = sh_m + NW * 16;                             // [NW][16]
+    float* sh_o = sh_l + NW * 16;                             // [NW][16][D]
+    if (g4 == 0) {
+        sh_m[w * 16 + l16] = m_run;
+        sh_l[w * 16 + l16] = l_head;
     }
-    if (slot == 0) {
 #pragma unroll
-        for (int hh = 0; hh < HG; ++hh) {
-            if (dl == 0) {
-                sh_m[w][hh] = m[hh];
-                sh_l[w][hh] = l[hh];
-            }
+    for (int dm = 0; dm < DB; ++dm)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sh_o[w][hh][dl * 8 + i] = o[hh][i];
-        }
-    }
+        for (int r = 0; r < 4; ++r) sh_o[(w * 16 + l16) * D + dm * 16 + 4 * g4 + r] = oacc[dm][r];
     __syncthreads();
-    // merge the waves and write the chunk's partial result
-    for (int e = tid; e < HG * D; e += 256) {
+    for (int e = tid; e < nh * D; e += 256) {
         const int hh = e / D, d = e % D;
-        float mm = sh_m[0][hh], ll = sh_l[0][hh], oo = sh_o[0][hh][d];
+        float mm = kNegInf;
 #pragma unroll
-        for (int ww = 1; ww < NW; ++ww) merge_state<1>(mm, ll, &oo, sh_m[ww][hh], sh_l[ww][hh], &sh_o[ww][hh][d]);
+        for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, sh_m[ww * 16 + hh]);
+        const float base = (mm == kNegInf) ? 0.f : mm;
+        float ll = 0.f, oo = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            const float mw = sh_m[ww * 16 + hh];
+            const float a = (mw == kNegInf) ? 0.f : fast_exp2(mw - base);
+            ll += a * sh_l[ww * 16 + hh];
+            oo += a * sh_o[(ww * 16 + hh) * D + d];
+        }
         const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
         p.part_o[row * D + d] = ll > 0.f ? oo / ll : 0.f;
         if (d == 0) p.part_lse[row] = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
@@ -287,8 +401,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p)
     if (p.lse && lane == 0) p.lse[row] = lse;
 }
 
-template <int D, int HG>
-hipError_t launch_split(const DecodeArgs& a, hipStream_t stream)
+template <int D>
+hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
 {
     SplitParams p;
     p.q = static_cast<const uint16_t*>(a.q);
@@ -302,22 +416,12 @@ hipError_t launch_split(const DecodeArgs& a, hipStream_t stream)
     p.N_max = a.N_max;
     p.S = a.num_splits;
     p.rep = a.H / a.H_kv;
-    p.c = a.scale * kLog2e;
-    if ((long long)a.H / HG > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_split_kernel<D, HG>), dim3(a.num_splits, a.H / HG, a.B), dim3(256), 0, stream, p);
-    return hipGetLastError();
-}
-
-template <int D>
-hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
-{
-    const int rep = a.H / a.H_kv;
-    // heads per workgroup: the largest of 8, 4, 2, 1 dividing H/H_kv
-    hipError_t e;
-    if (rep % 8 == 0) e = launch_split<D, 8>(a, stream);
-    else if (rep % 4 == 0) e = launch_split<D, 4>(a, stream);
-    else if (rep % 2 == 0) e = launch_split<D, 2>(a, stream);
-    else e = launch_split<D, 1>(a, stream);
+    p.ngrp = (p.rep + 15) / 16;               // groups of up to 16 query heads per KV head
+    p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
+    const long long gy = (long long)a.H_kv * p.ngrp;
+    if (gy > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     CombineParams cp{a.part_o, a.part_lse, static_cast<uint16_t*>(a.o), a.lse, a.B * a.H, a.num_splits};
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((cp.rows + 3) / 4), dim3(256), 0, stream, cp);
