@@ -62,6 +62,9 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+// cache policy of the K/V stream: non-temporal (each byte is used once; the
+// hint lets the memory system stream it rather than keep it cached)
+constexpr int kStreamPolicy = 2;
 
 struct SplitParams {
     const uint16_t* q;
@@ -70,7 +73,7 @@ struct SplitParams {
     const int* seq_lens;
     float* part_o;
     float* part_lse;
-    int H, H_kv, N_max, S, rep, ngrp;
+    int B, H, H_kv, N_max, S, rep, ngrp;
     float c;      // scale * log2(e), > 0
 };
 
@@ -169,6 +172,30 @@ __device__ __forceinline__ void lds_read_vt4(i16x4 (&a)[4], const unsigned (&p)[
                  : "memory");
 }
 
+__device__ __forceinline__ int clamped_len(const SplitParams& p, int b)
+{
+    return min(max(p.seq_lens[b], 0), p.N_max);   // never outside the cache
+}
+
+// Workgroups are dispatched in index order with blockIdx.z slowest, so z picks
+// the sequence by rank of length, longest first: the largest chunks start
+// first and the grid drains on the shortest ones.  Ranks order by length
+// (descending), then index, so they are a permutation of 0..B-1.  Batches of
+// more than 64 sequences keep index order.
+__device__ __forceinline__ int sequence_for(const SplitParams& p, int z)
+{
+    if (p.B > 64) return z;
+    const int lane = threadIdx.x & 63;
+    const int mine = lane < p.B ? clamped_len(p, lane) : -1;
+    int rank = 0;
+    for (int j = 0; j < p.B; ++j) {
+        const int lj = clamped_len(p, j);
+        rank += (lj > mine) || (lj == mine && j < lane);
+    }
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < p.B && rank == z);
+    return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
 {
@@ -189,14 +216,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     const int c = blockIdx.x;
     const int g = blockIdx.y / p.ngrp;
     const int hg = blockIdx.y % p.ngrp;
-    const int b = blockIdx.z;
+    const int b = sequence_for(p, blockIdx.z);
     const int h0 = g * p.rep + hg * 16;      // first query head of the group
     const int nh = min(16, p.rep - hg * 16); // heads in the group
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
 
-    const int len = min(max(p.seq_lens[b], 0), p.N_max);   // never outside the cache
+    const int len = clamped_len(p, b);
     const int L = (len + p.S - 1) / p.S;
     const int j0 = c * L;
     const int nkeys = max(0, min(j0 + L, len) - j0);
@@ -224,8 +251,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         char* dst = wl + s * 2 * TILEB;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_off[i], 0, 0, 0);
-            fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_off[i], 0, 0, 0);
+            fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_off[i], 0, 0, kStreamPolicy);
+            fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_off[i], 0, 0, kStreamPolicy);
         }
     };
 
@@ -361,38 +388,77 @@ struct CombineParams {
 };
 
 // One wave per (b, h) row: merge the S chunk summaries by their log-sum-exp.
+// Lane l owns output elements PER*l .. PER*l+PER-1 and holds the log-sum-exps
+// (then the weights) of chunks l, l+64, l+128, l+192; the chunk partials are
+// read in batches of 8 independent loads, the first batch in flight while the
+// log-sum-exps are reduced, so a row costs a few memory round trips rather than
+// one per chunk.
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p)
 {
     constexpr int PER = D / 64;          // output elements per lane
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    constexpr int BATCH = 8;
+    constexpr int KMAX = 4;              // S <= 256 = 4 x 64
+    typedef float vecP __attribute__((ext_vector_type(PER)));
+    const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
     if (row >= p.rows) return;
-    const float* lse_c = p.part_lse + (size_t)row * p.S;
+    const int S = p.S;                   // 1..256; chunk indices past S are clamped and weigh 0
+    const float* lse_c = p.part_lse + (size_t)row * S;
+    const vecP* oc = reinterpret_cast<const vecP*>(p.part_o + (size_t)row * S * D) + lane;   // chunk c at oc[c * 64]
+
+    vecP first[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) first[u] = oc[(size_t)min(u, S - 1) * 64];
+
+    float lv[KMAX];
     float mx = kNegInf;
-    for (int c = lane; c < p.S; c += 64) mx = fmaxf(mx, lse_c[c]);
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+        const int c = 64 * k + lane;
+        lv[k] = (64 * k < S) ? lse_c[min(c, S - 1)] : kNegInf;
+        lv[k] = c < S ? lv[k] : kNegInf;
+        mx = fmaxf(mx, lv[k]);
+    }
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) mx = fmaxf(mx, __shfl_xor(mx, x));
     float sum = 0.f;
-    if (mx != kNegInf)
-        for (int c = lane; c < p.S; c += 64) sum += exp2f((lse_c[c] - mx) * kLog2e);
+    if (mx != kNegInf) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) sum += lv[k] == kNegInf ? 0.f : exp2f((lv[k] - mx) * kLog2e);
+    }
 #pragma unroll
     for (int x = 32; x >= 1; x >>= 1) sum += __shfl_xor(sum, x);
     const float lse = (mx == kNegInf || sum <= 0.f) ? kNegInf : mx + logf(sum);
-    float acc[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) acc[i] = 0.f;
+
+    vecP acc = {};
     if (lse != kNegInf) {
-        const float* oc = p.part_o + (size_t)row * p.S * D + lane * PER;
-        for (int c = 0; c < p.S; ++c) {
-            const float wgt = exp2f((lse_c[c] - lse) * kLog2e);
+        // chunk weights exp(lse_c - lse); an empty chunk (lse_c = -inf) weighs 0
+        float wt[KMAX];
 #pragma unroll
-            for (int i = 0; i < PER; ++i) acc[i] = __builtin_fmaf(wgt, oc[(size_t)c * D + i], acc[i]);
+        for (int k = 0; k < KMAX; ++k) wt[k] = lv[k] == kNegInf ? 0.f : exp2f((lv[k] - lse) * kLog2e);
+        auto weight = [&](int c) __attribute__((always_inline)) {   // c uniform, < S
+            float r = 0.f;
+#pragma unroll
+            for (int k = 0; k < KMAX; ++k)
+                if ((c >> 6) == k) r = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wt[k]), c & 63));
+            return r;
+        };
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u)
+            if (u < S) acc += weight(u) * first[u];
+        for (int c0 = BATCH; c0 < S; c0 += BATCH) {
+            vecP v[BATCH];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) v[u] = oc[(size_t)min(c0 + u, S - 1) * 64];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u)
+                if (c0 + u < S) acc += weight(c0 + u) * v[u];
         }
     }
     uint16_t* dst = p.o + (size_t)row * D + lane * PER;
-    if (PER == 2) {
-        const bf16x2 t = __builtin_convertvector((f32x2{acc[0], acc[PER - 1]}), bf16x2);
+    if constexpr (PER == 2) {
+        const bf16x2 t = __builtin_convertvector((f32x2{acc[0], acc[1]}), bf16x2);
         *reinterpret_cast<bf16x2*>(dst) = t;
     } else {
         const bf16x2 t = __builtin_convertvector((f32x2{acc[0], 0.f}), bf16x2);
@@ -411,6 +477,7 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     p.seq_lens = a.seq_lens;
     p.part_o = a.part_o;
     p.part_lse = a.part_lse;
+    p.B = a.B;
     p.H = a.H;
     p.H_kv = a.H_kv;
     p.N_max = a.N_max;
