@@ -11,9 +11,8 @@
 // (toolsku.com) GQA code).
 //
 // gfx950 mapping (not from the pages, whose kernel targets other GPUs):
-//  * workgroup = NW waves, BM = 32*NW query rows, each wave owns 32 rows; at
-//    NW = 8 two waves share a SIMD, so one wave's softmax overlaps the other's
-//    matrix-core work;
+//  * workgroup = 8 waves, BM = 256 query rows, each wave owns 32 rows; two
+//    waves share each SIMD;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    (A = K fragment from LDS, B = Q fragment held in VGPRs for the whole
 //    kernel).  In the 32x32 accumulator layout lane l holds column l%32 -- one
@@ -25,13 +24,19 @@
 //    from the row-major V tile with the transposing LDS read ds_read_b64_tr_b16
 //    (two per MFMA: keys 4h..4h+3 and 8+4h..8+4h+3 of a 16-key step, which is
 //    the key order of the score accumulator);
-//  * K and V tiles go from global memory straight into LDS with
+//  * K and V tiles (64 keys) go from global memory straight into LDS with
 //    buffer_load_dwordx4 ... lds (no VGPR staging); rows past N_k read as 0
-//    through the buffer descriptor's range check and are masked.  Two LDS
-//    buffers: the next tile loads while the current one is used; one barrier
-//    per key block.  16-byte chunks of a row are XOR-swizzled so that both the
-//    K fragment reads and the transposing V reads are bank-conflict free on
-//    the 64-bank LDS;
+//    through the buffer descriptor's range check and are masked.  16-byte
+//    chunks of a row are XOR-swizzled so that both the K fragment reads and the
+//    transposing V reads are bank-conflict free on the 64-bank LDS;
+//  * the key loop runs in periods, one barrier each: in period j every wave
+//    reads K tile j and V tile j-1 while K tile j+1 and V tile j load into the
+//    other slots.  A wave's period has a matrix-core phase (O^T += V^T P^T of
+//    tile j-1, S^T of tile j) and a softmax phase (tile j's P).  Waves 0-3 run
+//    MFMA then softmax, waves 4-7 softmax then MFMA, so on each SIMD one wave's
+//    exponentials overlap the other wave's matrix-core work;
+//  * the matrix-core phase is a two-deep pipeline of steps of four MFMAs: the
+//    next step's LDS fragments are read before this step's MFMAs issue;
 //  * softmax in base 2 (scores scaled by scale*log2(e), v_exp_f32); the
 //    running max is only raised -- and O and l rescaled -- when a row's block
 //    maximum exceeds it by more than 8 (so every exp2 argument stays <= 8 and
@@ -89,6 +94,16 @@ struct Params {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// f(integral_constant<int, I>) for I = FIRST .. LAST-1, unrolled at compile time
+template <int FIRST, int LAST, typename F>
+__device__ __forceinline__ void static_for(F&& f)
+{
+    if constexpr (FIRST < LAST) {
+        f(std::integral_constant<int, FIRST>{});
+        static_for<FIRST + 1, LAST>(f);
+    }
+}
+
 // Buffer descriptor over `bytes` bytes at p (reads past the range return 0).
 __device__ __forceinline__ i32x4 make_rsrc(const void* p, unsigned bytes)
 {
@@ -138,6 +153,7 @@ __device__ __forceinline__ void decompose(int id, const Params& p, bool causal, 
 template <int D, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 {
+    static_assert(NW == 8, "the two wave groups pair up on the four SIMDs");
     constexpr int BM = NW * 32;              // query rows per workgroup
     constexpr int NTHR = NW * 64;
     constexpr int BN = 64;                   // keys per LDS tile
@@ -151,14 +167,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     static_assert(TILE % (NTHR * 16) == 0, "tile must be a whole number of wave loads");
     static_assert(D % 32 == 0, "tile shape");
 
-    // [buffer][K, V][tile]
-    __shared__ __attribute__((aligned(1024))) char lds[2 * 2 * TILE];
+    // [K slot 0, K slot 1, V slot 0, V slot 1]
+    __shared__ __attribute__((aligned(1024))) char lds[4 * TILE];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int l32 = lane & 31;
     const int half = lane >> 5;
+    const int role = w >> 2;                 // waves w and w+4 share a SIMD
 
     int qb, h, b;
     decompose(blockIdx.x, p, CAUSAL, qb, h, b);
@@ -177,6 +194,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     if (CAUSAL) kend = min(p.N_k, q0 + BM + off);
     const int nkb = kend > 0 ? (kend + BN - 1) / BN : 0;
     const int last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
+    // tiles this wave computes: 0 .. nkb_w-1 (later ones lie after its last row)
+    int nkb_w = nkb;
+    if (CAUSAL) nkb_w = max(0, min(nkb, (qw0 + 31 + off) / BN + 1));
 
     // ---- tile loads: chunk position -> (row, global chunk)
     int ld_voff[LOADS];
@@ -186,19 +206,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         const int r = pos / CPR, cp = pos % CPR;
         ld_voff[i] = r * ROWB + swz<D>(r, cp) * 16;
     }
-    auto issue_tile = [&](int kb, int buf) {
+    auto issue = [&](const char* base, int kb, char* dst) __attribute__((always_inline)) {
         const int key0 = kb * BN;
         const unsigned bytes = (unsigned)min(BN, p.N_k - key0) * ROWB;
-        const i32x4 rk = make_rsrc(kbase + (size_t)key0 * ROWB, bytes);
-        const i32x4 rv = make_rsrc(vbase + (size_t)key0 * ROWB, bytes);
-        char* kt = lds + (buf * 2 + 0) * TILE;
-        char* vt = lds + (buf * 2 + 1) * TILE;
+        const i32x4 rs = make_rsrc(base + (size_t)key0 * ROWB, bytes);
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int wpos = (i * NTHR + w * 64) * 16;    // this wave's 1 KB slice
-            fa_raw_buffer_load_lds(rk, (LDS_AS void*)(kt + wpos), 16, ld_voff[i], 0, 0, 0);
-            fa_raw_buffer_load_lds(rv, (LDS_AS void*)(vt + wpos), 16, ld_voff[i], 0, 0, 0);
-        }
+        for (int i = 0; i < LOADS; ++i)
+            fa_raw_buffer_load_lds(rs, (LDS_AS void*)(dst + (i * NTHR + w * 64) * 16), 16, ld_voff[i], 0, 0, 0);
     };
 
     // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole kernel
@@ -243,34 +257,83 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     float m_run = kNegInf;      // running max (log2 units of the scaled scores)
     float nbase = 0.f;          // -m_run, or 0 while the row has seen no key
     float l_a = 0.f, l_b = 0.f; // this lane's part of the running sum (two chains)
+    f32x16 s[NT];               // S^T of the latest tile
+    bf16x8 pf[NT][2];           // P of the latest softmax-ed tile (bf16)
 
-    auto body = [&](int kb, auto bufc) {
-        constexpr int BUF = decltype(bufc)::value;
-        const char* kt_lds = lds + (BUF * 2 + 0) * TILE;
-        const char* vt_lds = lds + (BUF * 2 + 1) * TILE;
-        // tile kb must be in LDS for every wave; the other buffer must be free
-        __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0): this wave's loads landed
-        __syncthreads();
-        if (kb + 1 < nkb) issue_tile(kb + 1, BUF ^ 1);
-
-        const int key0 = kb * BN;
-        // wave-level causal skip: the whole tile lies after this wave's last row
-        if (CAUSAL && key0 > qw0 + 31 + off) return;
-        const bool need_mask = (key0 + BN > p.N_k) || (CAUSAL && key0 + BN - 1 > qw0 + off);
-
-        // ---- S^T = K Q^T for the BN keys of the tile (fp32 accumulate)
-        f32x16 s[NT];
+    // matrix-core phase of period j: O^T += V^T P^T for tile j-1 (steps
+    // 0 .. NPV-1) and S^T = K Q^T for tile j (steps NPV .. NSTEP-1).  Steps of
+    // up to 4 MFMAs run as a two-deep pipeline -- the LDS fragments of step
+    // i+1 are read while step i's MFMAs issue -- and scheduling fences between
+    // steps keep the compiler from hoisting every read (and its registers) to
+    // the top.
+    constexpr int NPV = NT * 2;              // 16-key steps of the PV product
+    constexpr int NS = KSTEPS / 2;           // pairs of d k-steps of the S product
+    constexpr int NSTEP = NPV + NS;
+    static_assert(DBLK <= 4, "four fragments per step");
+    struct Frags {
+        bf16x8 f[4];
+    };
+    auto load_step = [&](auto stc, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
+        constexpr int st = decltype(stc)::value;
+        Frags r;
+        bf16x8* f = r.f;
+        if constexpr (st < NPV) {
+            const char* vp = vt_lds + ((st >> 1) * 32 + (st & 1) * 16) * ROWB;
 #pragma unroll
-        for (int kt = 0; kt < NT; ++kt) {
-            s[kt] = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt_lds + kt * 32 * ROWB + k_off[ks]);
-                s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kt], 0, 0, 0);
+            for (int dm = 0; dm < DBLK; ++dm) {
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[0][dm]));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[1][dm]));
+                f[dm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
+        } else {
+            constexpr int q = st - NPV;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                f[i] = *reinterpret_cast<const bf16x8*>(kt_lds + (i & 1) * 32 * ROWB + k_off[2 * q + (i >> 1)]);
         }
-
-        // ---- mask keys past this row's last visible key (diagonal / tail tiles)
+        return r;
+    };
+    auto mma_step = [&](auto stc, const Frags& fr) __attribute__((always_inline)) {
+        constexpr int st = decltype(stc)::value;
+        const bf16x8* f = fr.f;
+        if constexpr (st < NPV) {
+#pragma unroll
+            for (int dm = 0; dm < DBLK; ++dm)
+                oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[dm], pf[st >> 1][st & 1], oacc[dm], 0, 0, 0);
+        } else {
+            constexpr int q = st - NPV;
+            if constexpr (q == 0) {
+                s[0] = f32x16{};
+                s[1] = f32x16{};
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[2 * q + (i >> 1)], s[i & 1], 0, 0, 0);
+        }
+    };
+    auto run_steps = [&](auto firstc, auto lastc, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
+        constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value;
+        Frags cur = load_step(std::integral_constant<int, FIRST>{}, kt_lds, vt_lds);
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<FIRST, LAST>([&](auto stc) __attribute__((always_inline)) {
+            constexpr int st = decltype(stc)::value;
+            Frags nxt;
+            if constexpr (st + 1 < LAST) {
+                nxt = load_step(std::integral_constant<int, st + 1>{}, kt_lds, vt_lds);
+                // reads before MFMAs: left in one region the scheduler sinks
+                // them below the MFMAs to reuse their registers, and the
+                // read latency lands on every step
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            mma_step(stc, cur);
+            if constexpr (st + 1 < LAST) cur = nxt;
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    };
+    // vector phase: mask, online softmax and P for tile j (held in s)
+    auto softmax_phase = [&](int j) __attribute__((always_inline)) {
+        const int key0 = j * BN;
+        const bool need_mask = (key0 + BN > p.N_k) || (CAUSAL && key0 + BN - 1 > qw0 + off);
         if (need_mask) {
             const int lim = last_vis - key0 - 4 * half;
 #pragma unroll
@@ -279,9 +342,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 for (int r = 0; r < 16; ++r)
                     if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][r] = kNegInf;
         }
-
-        // ---- online softmax: row max of the tile, raise the running max only
-        //      when it grows by more than the slack (then rescale O and l)
+        // row max of the tile; the running max is raised only when it grows by
+        // more than the slack (then O and l are rescaled)
         float mx = kNegInf;
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt)
@@ -302,10 +364,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             m_run = m_new;
             nbase = (m_new == kNegInf) ? 0.f : -m_new;
         }
-
-        // ---- P = exp2(c*s - m): summed in fp32 (the lse needs the unrounded
-        //      weights), rounded to bf16 as the B operand of O^T += V^T P^T
-        bf16x8 pf[NT][2];
+        // P = exp2(c*s - m): summed in fp32 (the lse needs the unrounded
+        // weights), rounded to bf16 as the B operand of O^T += V^T P^T
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
@@ -320,28 +380,79 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 }
                 pf[kt][s2] = __builtin_convertvector(t, bf16x8);
             }
-
-        // ---- O^T += V^T P^T
+        // the phase's results exist here: without this the compiler sinks the
+        // exponentials past the next barrier, next to the MFMAs that use them
 #pragma unroll
         for (int kt = 0; kt < NT; ++kt)
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) {
-                const char* vp = vt_lds + (kt * 32 + s2 * 16) * ROWB;
-#pragma unroll
-                for (int dm = 0; dm < DBLK; ++dm) {
-                    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[0][dm]));
-                    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[1][dm]));
-                    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-                    oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kt][s2], oacc[dm], 0, 0, 0);
-                }
-            }
+            for (int s2 = 0; s2 < 2; ++s2) asm volatile("" : "+v"(pf[kt][s2]));
+        asm volatile("" : "+v"(l_a), "+v"(l_b));
+        __builtin_amdgcn_sched_barrier(0);
     };
 
-    if (nkb > 0) issue_tile(0, 0);
-    for (int kb = 0; kb < nkb; kb += 2) {
-        body(kb, std::integral_constant<int, 0>{});
-        if (kb + 1 < nkb) body(kb + 1, std::integral_constant<int, 1>{});
+    // ---- periods j = 0 .. nkb.  In period j every wave reads K tile j and V
+    //      tile j-1 only, while K tile j+1 and V tile j load into the other
+    //      slots (K tile j in K slot j%2, V tile j in V slot j%2).  The two
+    //      waves that share a SIMD run the two phases in opposite order, so one
+    //      wave's softmax overlaps the other's matrix-core work:
+    //        waves 0-3:  MFMA(PV j-1, S j), softmax(j)
+    //        waves 4-7:  softmax(j-1), MFMA(PV j-1, S j)
+    //      A wave computes tiles 0 .. nkb_w-1: period 0 has no PV, period
+    //      nkb_w no S, and later periods only keep the barriers and loads.
+    //      Each role has its own loop (straight-line phases keep the register
+    //      allocation tight); both pass the same nkb+1 barriers.
+    // One period: the barrier, this period's tile loads into the free slots,
+    // then the role's phases (SM: 1 = softmax of tile j-1 before the MFMAs,
+    // 2 = softmax of tile j after them).  The slot pointers are restrict
+    // qualified: within a period the loads and the LDS reads touch different
+    // slots, and saying so keeps the compiler from waiting for the loads
+    // before the first read (their order across periods comes from the
+    // explicit wait and the barrier).
+    auto period = [&](int j, auto firstc, auto lastc, auto smc, char* __restrict__ kdst, char* __restrict__ vdst,
+                      const char* __restrict__ kt, const char* __restrict__ vt) __attribute__((always_inline)) {
+        constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value, SM = decltype(smc)::value;
+        __builtin_amdgcn_s_waitcnt(0x0f70);                   // vmcnt(0): this wave's loads landed
+        __syncthreads();
+        if (j + 1 < nkb) issue(kbase, j + 1, kdst);
+        if (j < nkb) issue(vbase, j, vdst);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (SM == 1) softmax_phase(j - 1);
+        if constexpr (FIRST < LAST) {
+            __builtin_amdgcn_s_setprio(1);           // matrix-core phase first when both waves are ready
+            run_steps(firstc, lastc, kt, vt);
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (SM == 2) softmax_phase(j);
+    };
+    // slots of period j: K tile j+1 and V tile j load, K tile j and V tile j-1
+    // are read; tile t lives in slot t % 2
+    auto run_period = [&](int j, auto firstc, auto lastc, auto smc) __attribute__((always_inline)) {
+        const int b = j & 1;
+        period(j, firstc, lastc, smc, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE, lds + b * TILE,
+               lds + (2 + (b ^ 1)) * TILE);
+    };
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using CNPV = std::integral_constant<int, NPV>;
+    using CNSTEP = std::integral_constant<int, NSTEP>;
+
+    if (nkb > 0) issue(kbase, 0, lds);
+    int j = 0;
+    if (nkb_w > 0) {
+        if (role == 0) {
+            run_period(0, CNPV{}, CNSTEP{}, C2{});
+            for (j = 1; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{});
+            run_period(j, C0{}, CNPV{}, C0{});            // j == nkb_w: PV of the last tile
+        } else {
+            run_period(0, CNPV{}, CNSTEP{}, C0{});
+            for (j = 1; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{});
+            run_period(j, C0{}, CNPV{}, C1{});
+        }
+        ++j;
     }
+    for (; j <= nkb; ++j) run_period(j, C0{}, C0{}, C0{});  // tiles after this wave's rows
 
     // ---- epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l)
     float l_tot;
