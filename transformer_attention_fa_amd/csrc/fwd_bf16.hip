@@ -273,61 +273,60 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     struct Frags {
         bf16x8 f[4];
     };
-    auto load_step = [&](auto stc, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
-        constexpr int st = decltype(stc)::value;
-        Frags r;
-        bf16x8* f = r.f;
+    // step st has nmma(st) MFMAs; part k of its fragments is fragment k
+    auto nmma = [](int st) constexpr { return st < NPV ? DBLK : 4; };
+    auto load_part = [&](auto stc, auto kc, Frags& r, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
+        constexpr int st = decltype(stc)::value, k = decltype(kc)::value;
         if constexpr (st < NPV) {
             const char* vp = vt_lds + ((st >> 1) * 32 + (st & 1) * 16) * ROWB;
-#pragma unroll
-            for (int dm = 0; dm < DBLK; ++dm) {
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[0][dm]));
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[1][dm]));
-                f[dm] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-            }
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[0][k]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS i16x4*)(vp + v_off[1][k]));
+            r.f[k] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         } else {
             constexpr int q = st - NPV;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                f[i] = *reinterpret_cast<const bf16x8*>(kt_lds + (i & 1) * 32 * ROWB + k_off[2 * q + (i >> 1)]);
+            r.f[k] = *reinterpret_cast<const bf16x8*>(kt_lds + (k & 1) * 32 * ROWB + k_off[2 * q + (k >> 1)]);
         }
-        return r;
     };
-    auto mma_step = [&](auto stc, const Frags& fr) __attribute__((always_inline)) {
-        constexpr int st = decltype(stc)::value;
-        const bf16x8* f = fr.f;
+    auto mma_part = [&](auto stc, auto kc, const Frags& r) __attribute__((always_inline)) {
+        constexpr int st = decltype(stc)::value, k = decltype(kc)::value;
         if constexpr (st < NPV) {
-#pragma unroll
-            for (int dm = 0; dm < DBLK; ++dm)
-                oacc[dm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[dm], pf[st >> 1][st & 1], oacc[dm], 0, 0, 0);
+            oacc[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.f[k], pf[st >> 1][st & 1], oacc[k], 0, 0, 0);
         } else {
             constexpr int q = st - NPV;
-            if constexpr (q == 0) {
-                s[0] = f32x16{};
-                s[1] = f32x16{};
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                s[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[i], qf[2 * q + (i >> 1)], s[i & 1], 0, 0, 0);
+            if constexpr (q == 0 && k < 2) s[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.f[k], qf[0], f32x16{}, 0, 0, 0);
+            else s[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.f[k], qf[2 * q + (k >> 1)], s[k & 1], 0, 0, 0);
         }
     };
+    // Steps FIRST .. LAST-1 as a pipeline: the fragments of step st+1 are read
+    // while step st's MFMAs run, one part after each MFMA, so the reads issue
+    // in the gaps while the wave waits for the matrix core; scheduling fences
+    // keep that order (left alone, the compiler groups the reads and sinks
+    // them below the MFMAs to reuse their registers, and the read latency or
+    // issue time lands on every step).
     auto run_steps = [&](auto firstc, auto lastc, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
         constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value;
-        Frags cur = load_step(std::integral_constant<int, FIRST>{}, kt_lds, vt_lds);
+        Frags cur;
+        static_for<0, nmma(FIRST)>([&](auto kc) __attribute__((always_inline)) {
+            load_part(firstc, kc, cur, kt_lds, vt_lds);
+        });
         __builtin_amdgcn_sched_barrier(0);
         static_for<FIRST, LAST>([&](auto stc) __attribute__((always_inline)) {
             constexpr int st = decltype(stc)::value;
+            constexpr int NM = nmma(st);
+            constexpr int NL = st + 1 < LAST ? nmma(st + 1) : 0;
             Frags nxt;
-            if constexpr (st + 1 < LAST) {
-                nxt = load_step(std::integral_constant<int, st + 1>{}, kt_lds, vt_lds);
-                // reads before MFMAs: left in one region the scheduler sinks
-                // them below the MFMAs to reuse their registers, and the
-                // read latency lands on every step
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            mma_step(stc, cur);
-            if constexpr (st + 1 < LAST) cur = nxt;
-            __builtin_amdgcn_sched_barrier(0);
+            static_for<0, (NM > NL ? NM : NL)>([&](auto kc) __attribute__((always_inline)) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (k < NM) {
+                    mma_part(stc, kc, cur);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                if constexpr (k < NL) {
+                    load_part(std::integral_constant<int, st + 1>{}, kc, nxt, kt_lds, vt_lds);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            });
+            if constexpr (NL > 0) cur = nxt;
         });
     };
     // vector phase: mask, online softmax and P for tile j (held in s)
