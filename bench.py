@@ -31,8 +31,8 @@ METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mha", choices=["mha", "gqa", "mqa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
@@ -77,8 +77,9 @@ def cpu_baseline(spec, n_batches):
     dt = time.perf_counter() - t0
     flops = roofline.attention_flops(sub.B, sub.H, sub.N_q, sub.N_k, sub.d, sub.causal)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"{n_batches} of {spec.B} sequences ({n_batches * spec.H} heads) of {spec.name}, "
-                      f"fp64, {dt:.2f} s wall"}
+            "sample": (f"the whole {spec.name} workload" if n_batches == spec.B else
+                       f"{n_batches} of {spec.B} sequences ({n_batches * spec.H} heads) of {spec.name}")
+                      + f", fp64, {dt:.2f} s wall"}
 
 
 def main():
@@ -168,7 +169,8 @@ def main():
         rec.update({"value": tflops, "unit": "TFLOP/s"})
         rec["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": roofline.PEAK_BF16_TFLOPS,
                            "unit": "TFLOP/s", "frac": tflops / roofline.PEAK_BF16_TFLOPS, "traffic": traffic,
-                           "kernel": "fwd_bf16_kernel", "launch_ms_avg": t_avg, "launch_ms_min": float(np.min(t_pf)),
+                           "kernel": "fwd_bf16_kernel", "launch_ms_avg": t_avg,
+                           "launch_ms_median": float(np.median(t_pf)), "launch_ms_min": float(np.min(t_pf)),
                            "flop_per_launch": flops}
         config["workload"] = pspec.name
         config["prefill"] = {"B": pspec.B, "H": pspec.H, "H_kv": pspec.H_kv, "N_q": pspec.N_q, "N_k": pspec.N_k,
@@ -179,7 +181,8 @@ def main():
         kv_bytes = roofline.decode_kv_bytes(dspec.H_kv, dspec.d, seq_lens)
         gbps = kv_bytes / (t_avg_d * 1e-3) / 1e9
         rec["decode"] = {"value": gbps, "unit": "GB/s", "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS,
-                         "ms_avg": t_avg_d, "ms_min": float(np.min(t_dc)), "kv_bytes": kv_bytes,
+                         "ms_avg": t_avg_d, "ms_median": float(np.median(t_dc)), "ms_min": float(np.min(t_dc)),
+                         "kv_bytes": kv_bytes,
                          "roofline": {"bound": "hbm", "achieved": gbps, "peak": roofline.PEAK_HBM_GBPS,
                                       "unit": "GB/s", "frac": gbps / roofline.PEAK_HBM_GBPS,
                                       "traffic": traffic_for(f"decode:{dspec.name}", ["decode.hip"]),
@@ -192,7 +195,7 @@ def main():
             rec.update({"value": gbps, "unit": "GB/s"})
     rec["config"] = config
     if do_prefill and not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(pspec, n_batches=max(1, min(pspec.B, 4)))
+        rec["cpu_baseline"] = cpu_baseline(pspec, n_batches=pspec.B)
     props = torch.cuda.get_device_properties(dev)
     rec["device"] = {"name": props.name, "cus": props.multi_processor_count,
                      "gcn_arch": getattr(props, "gcnArchName", "")}
