@@ -44,12 +44,12 @@ def load_library(path: str):
     """Open a compiled oracle library and declare its C signatures."""
     lib = ctypes.CDLL(path)
     vp, dp, lp, ip = ctypes.c_void_p, ctypes.c_double, ctypes.c_long, ctypes.c_int
-    lib.oracle_attention.argtypes = [vp, vp, vp, ip, vp, vp, lp, lp, lp, lp, lp, lp, dp, ip]
+    lib.oracle_attention.argtypes = [vp, vp, vp, ip, vp, vp, lp, lp, lp, lp, lp, lp, dp, ip, lp]
     lib.oracle_attention.restype = ip
     lib.oracle_attention_rows.argtypes = [vp, vp, vp, ip, vp, lp, vp, vp,
-                                          lp, lp, lp, lp, lp, lp, dp, ip]
+                                          lp, lp, lp, lp, lp, lp, dp, ip, lp]
     lib.oracle_attention_rows.restype = ip
-    lib.oracle_decode.argtypes = [vp, vp, vp, ip, vp, vp, vp, lp, lp, lp, lp, lp, dp]
+    lib.oracle_decode.argtypes = [vp, vp, vp, ip, vp, vp, vp, lp, lp, lp, lp, lp, dp, lp]
     lib.oracle_decode.restype = ip
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = ip
@@ -92,8 +92,18 @@ def _prep(*arrays):
     return arrays, codes.pop()
 
 
-def attention(q, k, v, scale: float, causal: bool):
-    """O [B,H,N_q,d] and LSE [B,H,N_q] in fp64 for q [B,H,N_q,d], k/v [B,H_kv,N_k,d]."""
+def _window(window, causal=True) -> int:
+    if window is None or window <= 0:
+        return 0
+    if not causal:
+        raise ValueError("a sliding window is causal")
+    return int(window)
+
+
+def attention(q, k, v, scale: float, causal: bool, window=None):
+    """O [B,H,N_q,d] and LSE [B,H,N_q] in fp64 for q [B,H,N_q,d], k/v [B,H_kv,N_k,d].
+    ``window`` (keys, causal only): row i sees the ``window`` keys ending at its
+    last causally visible key."""
     (q, k, v), code = _prep(q, k, v)
     B, H, N_q, d = q.shape
     Bk, H_kv, N_k, dk = k.shape
@@ -102,13 +112,14 @@ def attention(q, k, v, scale: float, causal: bool):
     o = np.empty((B, H, N_q, d), np.float64)
     lse = np.empty((B, H, N_q), np.float64)
     rc = _load().oracle_attention(_ptr(q), _ptr(k), _ptr(v), code, _ptr(o), _ptr(lse),
-                                  B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)))
+                                  B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)),
+                                  _window(window, causal))
     if rc != 0:
         raise ValueError(f"oracle_attention failed with code {rc}")
     return o, lse
 
 
-def attention_rows(q, k, v, rows, scale: float, causal: bool):
+def attention_rows(q, k, v, rows, scale: float, causal: bool, window=None):
     """O and LSE for the (b, h, i) query rows listed in ``rows`` only."""
     (q, k, v), code = _prep(q, k, v)
     B, H, N_q, d = q.shape
@@ -119,14 +130,15 @@ def attention_rows(q, k, v, rows, scale: float, causal: bool):
     lse = np.empty((n,), np.float64)
     rc = _load().oracle_attention_rows(_ptr(q), _ptr(k), _ptr(v), code, _ptr(rows), n,
                                        _ptr(o), _ptr(lse), B, H, H_kv, N_q, N_k, d,
-                                       float(scale), int(bool(causal)))
+                                       float(scale), int(bool(causal)), _window(window, causal))
     if rc != 0:
         raise ValueError(f"oracle_attention_rows failed with code {rc}")
     return o, lse
 
 
-def decode(q, k_cache, v_cache, seq_lens, scale: float):
-    """One decode step: O [B,H,d] and LSE [B,H] in fp64."""
+def decode(q, k_cache, v_cache, seq_lens, scale: float, window=None):
+    """One decode step: O [B,H,d] and LSE [B,H] in fp64; with ``window`` the
+    query sees only the last ``window`` cached rows."""
     (q, k_cache, v_cache), code = _prep(q, k_cache, v_cache)
     B, H, d = q.shape
     _, H_kv, N_max, _ = k_cache.shape
@@ -136,7 +148,7 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float):
     o = np.empty((B, H, d), np.float64)
     lse = np.empty((B, H), np.float64)
     rc = _load().oracle_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), code, _ptr(lens),
-                               _ptr(o), _ptr(lse), B, H, H_kv, N_max, d, float(scale))
+                               _ptr(o), _ptr(lse), B, H, H_kv, N_max, d, float(scale), _window(window))
     if rc != 0:
         raise ValueError(f"oracle_decode failed with code {rc}")
     return o, lse

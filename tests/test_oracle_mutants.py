@@ -22,12 +22,18 @@ MUTANTS = {
     "dropped_scale": ("s[j] = scale * acc;", "s[j] = acc;"),
     "lse_without_max": ("*lse_out = m + log(z);", "*lse_out = log(z);"),
     "lse_log2": ("*lse_out = m + log(z);", "*lse_out = m + log2(z);"),
-    "no_normalisation": ("for (j = 0; j < n_visible; ++j) s[j] /= z;", ""),
+    "no_normalisation": ("for (j = first; j < n_visible; ++j) s[j] /= z;", ""),
     "exp_sign_flipped": ("s[j] = exp(s[j] - m);", "s[j] = exp(m - s[j]);"),
     "values_reversed": ("size_t row = kv_off + (size_t)j * (size_t)d;",
                         "size_t row = kv_off + (size_t)(n_visible - 1 - j) * (size_t)d;"),
     "max_is_first_score": ("if (s[j] > m) m = s[j];", "if (s[j] > m) m = m;"),
-    "decode_reads_padding": ("kv_off, len, len, d, scale, s,", "kv_off, N_max, N_max, d, scale, s,"),
+    "decode_reads_padding": ("kv_off, len, first, len, d, scale, s,", "kv_off, N_max, first, N_max, d, scale, s,"),
+    "window_off_by_one": ("long f = i + (n_k - n_q) - w + 1;", "long f = i + (n_k - n_q) - w;"),
+    "window_top_left": ("long f = i + (n_k - n_q) - w + 1;", "long f = i - w + 1;"),
+    "window_ignored": ("if (w <= 0) return 0;", "return 0;"),
+    "decode_window_off_by_one": ("long first = window > 0 && len > window ? len - window : 0;",
+                                 "long first = window > 0 && len > window ? len - window + 1 : 0;"),
+    "decode_window_ignored": ("long first = window > 0 && len > window ? len - window : 0;", "long first = 0;"),
     "empty_row_lse_zero": ("*lse_out = -INFINITY;", "*lse_out = 0.0;"),
 }
 
@@ -49,7 +55,10 @@ def _pin_suite():
             calls.append(lambda c=causal, s=shape: P.test_brute_force_tiny(s, c))
     calls += [P.test_causal_row_zero_and_single_key, P.test_one_dominant_key_at_extreme_scale, P.test_rows_with_no_visible_key,
               P.test_joint_key_value_permutation, P.test_scale_is_applied_to_scores,
-              P.test_matches_torch_sdpa, P.test_decode_equals_single_query_prefill_and_split_merge]
+              P.test_matches_torch_sdpa, P.test_decode_equals_single_query_prefill_and_split_merge,
+              P.test_window_matches_pages_example, P.test_brute_force_tiny_window, P.test_decode_window]
+    for nq, nk, w in ((9, 9, 3), (4, 11, 5), (11, 4, 2), (6, 6, 1)):
+        calls.append(lambda a=nq, b=nk, c=w: P.test_window_zero_query_closed_form(a, b, c))
     return calls
 
 

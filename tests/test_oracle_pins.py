@@ -372,3 +372,158 @@ def test_decode_rejects_bad_lengths():
         oracle.decode(q, kc, kc, [0, 3], 1.0)
     with pytest.raises(ValueError):
         oracle.decode(q, kc, kc, [6, 3], 1.0)
+
+
+# --------------------------------------------------------------------------
+# P-j: sliding window ("Attention variants" §4): each token looks only at the
+# W most recent tokens, itself included.  The window ends at the row's last
+# causally visible key, i + (N_k - N_q).
+# --------------------------------------------------------------------------
+def window_range(i, n_q, n_k, w):
+    """First and one-past-last visible key of row i, written from the page's example."""
+    hi = min(n_k, i + (n_k - n_q) + 1)
+    lo = max(0, i + (n_k - n_q) - w + 1)
+    return lo, max(lo, hi)
+
+
+def _golden_window_rows():
+    import os
+    rows = {}
+    path = os.path.join(os.path.dirname(__file__), "golden", "sliding_window_example.txt")
+    for line in open(path):
+        line = line.split("#")[0].strip()
+        if line:
+            qi, keys = line.split(":")
+            rows[int(qi)] = [int(x) for x in keys.split()]
+    return rows
+
+
+def test_window_matches_pages_example():
+    # N = 8, W = 3; Q = 0 and V = identity: row i of O is uniform over exactly
+    # the keys row i sees, so its support is the visible set
+    n, w = 8, 3
+    q = np.zeros((1, 1, n, n))
+    k = rand((1, 1, n, n), 121)
+    v = np.eye(n).reshape(1, 1, n, n)
+    o, lse = oracle.attention(q, k, v, 1.0, True, window=w)
+    golden = _golden_window_rows()
+    assert golden, "fixture is empty"
+    for i, keys in golden.items():
+        assert list(np.nonzero(o[0, 0, i])[0]) == keys
+    for i in range(n):
+        support = list(np.nonzero(o[0, 0, i])[0])
+        assert support == list(range(max(0, i - w + 1), i + 1))
+        assert abs(lse[0, 0, i] - math.log(len(support))) <= TOL
+
+
+@pytest.mark.parametrize("n_q,n_k,w", [(9, 9, 3), (4, 11, 5), (11, 4, 2), (6, 6, 1), (5, 12, 20)])
+def test_window_zero_query_closed_form(n_q, n_k, w):
+    d = 5
+    q = np.zeros((2, 2, n_q, d))
+    k = rand((2, 2, n_k, d), 122)
+    v = rand((2, 2, n_k, d), 123)
+    o, lse = oracle.attention(q, k, v, 0.4, True, window=w)
+    for b in range(2):
+        for h in range(2):
+            for i in range(n_q):
+                lo, hi = window_range(i, n_q, n_k, w)
+                if hi == lo:
+                    assert np.all(o[b, h, i] == 0) and np.isneginf(lse[b, h, i])
+                    continue
+                np.testing.assert_allclose(o[b, h, i], v[b, h, lo:hi].mean(axis=0), atol=TOL, rtol=0)
+                assert abs(lse[b, h, i] - math.log(hi - lo)) <= TOL
+
+
+@pytest.mark.parametrize("n_q,n_k", [(7, 7), (3, 10), (10, 3)])
+def test_window_covering_the_keys_is_causal(n_q, n_k):
+    q, k, v = rand((1, 4, n_q, 6), 124), rand((1, 2, n_k, 6), 125), rand((1, 2, n_k, 6), 126)
+    o_c, l_c = oracle.attention(q, k, v, 0.5, True)
+    for w in (n_k + n_q, n_k + max(0, n_q - n_k)):
+        o_w, l_w = oracle.attention(q, k, v, 0.5, True, window=w)
+        np.testing.assert_array_equal(o_w, o_c)
+        np.testing.assert_array_equal(l_w, l_c)
+
+
+@pytest.mark.parametrize("n_q,n_k", [(6, 6), (3, 8)])
+def test_window_of_one_is_the_diagonal_key(n_q, n_k):
+    q, k, v = rand((1, 2, n_q, 7), 127), rand((1, 2, n_k, 7), 128), rand((1, 2, n_k, 7), 129)
+    o, lse = oracle.attention(q, k, v, 0.3, True, window=1)
+    off = n_k - n_q
+    for h in range(2):
+        for i in range(n_q):
+            j = i + off
+            np.testing.assert_allclose(o[0, h, i], v[0, h, j], atol=TOL, rtol=0)
+            assert abs(lse[0, h, i] - 0.3 * float(q[0, h, i] @ k[0, h, j])) <= TOL
+
+
+@pytest.mark.parametrize("n_q,n_k,w", [(12, 12, 4), (5, 13, 6), (13, 5, 3)])
+def test_window_matches_torch_masked_softmax(n_q, n_k, w):
+    import torch
+    q, k, v = rand((2, 4, n_q, 8), 131), rand((2, 2, n_k, 8), 132), rand((2, 2, n_k, 8), 133)
+    o, lse = oracle.attention(q, k, v, 0.35, True, window=w)
+    rep = 2
+    kt = torch.from_numpy(np.repeat(k, rep, axis=1))
+    vt = torch.from_numpy(np.repeat(v, rep, axis=1))
+    s = torch.from_numpy(q) @ kt.transpose(-1, -2) * 0.35
+    ii = torch.arange(n_q).view(-1, 1)
+    jj = torch.arange(n_k).view(1, -1)
+    last = ii + (n_k - n_q)
+    keep = (jj <= last) & (jj >= last - w + 1)
+    s = s.masked_fill(~keep, float("-inf"))
+    ref_l = torch.logsumexp(s, dim=-1).numpy()
+    ref_o = (torch.softmax(s, dim=-1) @ vt).numpy()
+    fin = np.isfinite(ref_l)
+    assert np.all(np.isneginf(lse[~fin])) and np.all(o[~fin] == 0)
+    np.testing.assert_allclose(o[fin], ref_o[fin], atol=1e-12, rtol=0)
+    np.testing.assert_allclose(lse[fin], ref_l[fin], atol=1e-12, rtol=0)
+
+
+def test_brute_force_tiny_window():
+    B, H, H_kv, n_q, n_k, d, w = 1, 2, 1, 4, 6, 3, 2
+    q, k, v = rand((B, H, n_q, d), 134), rand((B, H_kv, n_k, d), 135), rand((B, H_kv, n_k, d), 136)
+    o, lse = oracle.attention(q, k, v, 0.9, True, window=w)
+    for h in range(H):
+        for i in range(n_q):
+            keys = [j for j in range(n_k) if i + n_k - n_q - w + 1 <= j <= i + n_k - n_q]
+            s = {j: 0.9 * sum(q[0, h, i, t] * k[0, 0, j, t] for t in range(d)) for j in keys}
+            m = max(s.values())
+            z = sum(math.exp(s[j] - m) for j in keys)
+            for t in range(d):
+                ref = sum(math.exp(s[j] - m) / z * v[0, 0, j, t] for j in keys)
+                assert abs(o[0, h, i, t] - ref) <= TOL
+            assert abs(lse[0, h, i] - (m + math.log(z))) <= TOL
+
+
+def test_window_needs_causal():
+    q = rand((1, 1, 3, 2), 137)
+    with pytest.raises(ValueError):
+        oracle.attention(q, q, q, 1.0, False, window=2)
+
+
+def test_decode_window():
+    B, H, H_kv, N_max, d = 3, 4, 2, 40, 6
+    rng = np.random.default_rng(138)
+    k = rng.standard_normal((B, H_kv, N_max, d))
+    v = rng.standard_normal((B, H_kv, N_max, d))
+    lens = np.array([1, 17, 40], np.int32)
+    k[0, :, 1:] = np.nan
+    v[0, :, 1:] = np.nan
+    k[1, :, 17:] = np.nan
+    v[1, :, 17:] = np.nan
+    for w in (1, 5, 17, 100):
+        # Q = 0: the mean of the last min(w, len) rows, lse = ln of their number
+        o, lse = oracle.decode(np.zeros((B, H, d)), k, v, lens, 0.5, window=w)
+        for b in range(B):
+            n = min(w, int(lens[b]))
+            for h in range(H):
+                g = h // (H // H_kv)
+                np.testing.assert_allclose(o[b, h], v[b, g, lens[b] - n:lens[b]].mean(axis=0), atol=TOL, rtol=0)
+                assert abs(lse[b, h] - math.log(n)) <= TOL
+        # and a real query equals single-query prefill with the same window
+        q = rng.standard_normal((B, H, d))
+        o, lse = oracle.decode(q, k, v, lens, 0.5, window=w)
+        for b in range(B):
+            L = int(lens[b])
+            o1, l1 = oracle.attention(q[b:b + 1, :, None, :], k[b:b + 1, :, :L], v[b:b + 1, :, :L], 0.5, True, window=w)
+            np.testing.assert_allclose(o[b], o1[0, :, 0], atol=TOL, rtol=0)
+            np.testing.assert_allclose(lse[b], l1[0, :, 0], atol=TOL, rtol=0)
