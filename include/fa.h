@@ -15,6 +15,7 @@
  *       §2 MQA/GQA and the gqa_attention snippet (q [B,H,N,d_k], k/v [B,G,N,d_k],
  *          rep = H/G, repeat_interleave on the head axis, scores / sqrt(d_k)),
  *       §3 FlashAttention tiling and online softmax (exact, not approximate),
+ *       §4 sliding-window attention (each token sees the W most recent tokens),
  *       §5.5 causal block skip, §7 decode is memory-bandwidth bound,
  *       troubleshooting list: H must be a multiple of G.
  *  [ME] "Attention mechanism evolution: MHA -> MLA, Flash Attention" (toolsku.com)
@@ -85,6 +86,21 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    float scale, int causal, hipStream_t stream);
 
 /*
+ * fa_fwd_window -- fa_fwd with a sliding-window causal mask [AV §4: each token
+ * looks only at the W most recent tokens, itself included].  Query row i sees
+ * key j iff  i + (N_k - N_q) - window + 1 <= j <= i + (N_k - N_q): the window
+ * ends at the row's last causally visible key.  Key tiles wholly outside every
+ * row's window are neither loaded nor computed, so the cost grows with
+ * N_q * window rather than N_q * N_k.
+ *   window >= 1 (keys); a window of at least N_k + max(0, N_q - N_k) equals
+ *          fa_fwd with causal = 1.  window < 1: FA_ERR_INVALID_ARGUMENT.
+ *   Other arguments, layouts and errors as fa_fwd (the mask is always causal).
+ */
+fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int H_kv, int N_q, int N_k, int d,
+                          float scale, int window, hipStream_t stream);
+
+/*
  * fa_fwd_f32 -- the same operation with fp32 inputs and fp32 output
  * (fp32 arithmetic throughout).  Arguments and semantics as fa_fwd.
  */
@@ -133,6 +149,21 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       int B, int H, int H_kv, int N_max, int d, float scale,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
+
+/*
+ * fa_decode_window -- fa_decode where the query sees only the last `window`
+ * cached rows of its sequence, keys [max(0, seq_lens[b] - window),
+ * seq_lens[b]) [AV §4 sliding window; for the newest token the window ends
+ * at the cache's last row].  Those keys are cut into num_splits chunks as in
+ * fa_decode; nothing before them is read.
+ *   window >= 1; window < 1: FA_ERR_INVALID_ARGUMENT.  Other arguments,
+ *   workspace and errors as fa_decode (same workspace size).
+ */
+fa_status_t fa_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                             const int* seq_lens, void* o, float* lse,
+                             int B, int H, int H_kv, int N_max, int d, float scale,
+                             int window, int num_splits, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
 
 /* Static text for a status code. */
 const char* fa_status_string(fa_status_t s);

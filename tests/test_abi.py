@@ -84,7 +84,7 @@ FWD_CASES = [
 ]
 
 
-@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32"])
+@pytest.mark.parametrize("fn", ["fa_fwd", "fa_fwd_f32", "fa_fwd_window"])
 @pytest.mark.parametrize("name,change,expect", FWD_CASES, ids=[c[0] for c in FWD_CASES])
 def test_fwd_rejects_before_launch(lib, fn, name, change, expect):
     a = dict(GOOD_FWD, **change)
@@ -119,6 +119,21 @@ def test_decode_rejects_before_launch(lib, name, change, expect):
                        a["N_max"], a["d"], a["scale"], a["S"], a["ws"], a["ws_bytes"], None)
     assert st == expect, (name, st, lib.fa_last_error())
     assert lib.fa_last_error()
+    st = lib.fa_decode_window(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"],
+                              a["N_max"], a["d"], a["scale"], 64, a["S"], a["ws"], a["ws_bytes"], None)
+    assert st == expect, (name, st, lib.fa_last_error())
+
+
+@pytest.mark.parametrize("window", [0, -1, -(1 << 30)])
+def test_window_must_be_positive(lib, window):
+    a = GOOD_FWD
+    st = lib.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"], a["N_q"],
+                           a["N_k"], a["d"], a["scale"], window, None)
+    assert st == INVALID and b"window" in lib.fa_last_error()
+    d = GOOD_DEC
+    st = lib.fa_decode_window(d["q"], d["k"], d["v"], d["lens"], d["o"], d["lse"], d["B"], d["H"], d["H_kv"],
+                              d["N_max"], d["d"], d["scale"], window, d["S"], d["ws"], d["ws_bytes"], None)
+    assert st == INVALID and b"window" in lib.fa_last_error()
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -254,3 +254,96 @@ def test_decode_deterministic():
     o1, l1 = _decode_run(data, 16)
     o2, l2 = _decode_run(data, 16)
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+# ------------------------------------------------------------------ sliding window
+WINDOW_BF16 = [
+    # B, H, H_kv, N_q, N_k, d, window
+    (1, 4, 2, 300, 300, 128, 64),
+    (1, 4, 2, 300, 300, 128, 1),
+    (1, 2, 2, 333, 333, 128, 65),        # window edge inside a tile, ragged tail
+    (2, 2, 1, 517, 517, 64, 100),
+    (1, 2, 2, 200, 700, 128, 150),       # N_q < N_k: the window ends at i + 500
+    (1, 2, 1, 700, 300, 128, 50),        # N_q > N_k: leading rows see no key
+    (1, 4, 4, 1024, 1024, 128, 256),     # tile-aligned window
+    (1, 2, 1, 1000, 1000, 128, 700),
+]
+
+
+@pytest.mark.parametrize("shape", WINDOW_BF16, ids=lambda s: "x".join(map(str, s)))
+def test_fwd_window_full_compare(shape):
+    import torch
+    B, H, H_kv, N_q, N_k, d, w = shape
+    spec = _spec(B, H, H_kv, N_q, N_k, d, True, seed=23)
+    say(f"fa_fwd_window {spec.name} window={w}")
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    o, lse = api.fwd(q, k, v, causal=True, scale=spec.scale, window=w)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, True, window=w)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"window {w}")
+
+
+def test_fwd_window_covering_the_keys_equals_causal():
+    import torch
+    spec = _spec(2, 4, 2, 600, 600, 128, True, seed=29)
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    o_c, l_c = api.fwd(q, k, v, causal=True, scale=spec.scale)
+    o_w, l_w = api.fwd(q, k, v, causal=True, scale=spec.scale, window=600)
+    torch.cuda.synchronize()
+    assert torch.equal(o_c, o_w) and torch.equal(l_c, l_w)
+
+
+@pytest.mark.parametrize("window", [1, 15, 16, 17, 300, 5000])
+@pytest.mark.parametrize("num_splits", [1, 5, 16])
+def test_decode_window(window, num_splits):
+    import torch
+    spec = _small_decode_spec(H=8, H_kv=2, d=128, N_max=3000, B=6, seed=31)
+    lens = np.array([1, 2, 16, 17, 1200, 3000], np.int32)
+    data = inputs.decode_inputs(spec, seq_lens=lens)
+    # rows before each window are never read: poison them
+    k_c, v_c = data.k_cache.copy(), data.v_cache.copy()
+    for b, n in enumerate(lens):
+        k_c[b, :, :max(0, n - window)] = inputs.BF16_QNAN
+        v_c[b, :, :max(0, n - window)] = inputs.BF16_QNAN
+    q = bf16_to_device(data.q)
+    kc, vc = bf16_to_device(k_c), bf16_to_device(v_c)
+    o, lse = api.decode(q, kc, vc, torch.from_numpy(lens).cuda(), num_splits=num_splits, scale=spec.scale,
+                        window=window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, lens, spec.scale, window=window)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL,
+            label=f"window {window} S={num_splits}")
+
+
+@pytest.mark.parametrize("spec", [inputs.SWA_PREFILL, inputs.CHUNKED_PREFILL], ids=lambda s: s.name)
+def test_fwd_next_workloads_sampled(spec):
+    import torch
+    say(f"fa_fwd full-size workload {spec.name}")
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    o, lse = api.fwd(q, k, v, causal=spec.causal, scale=spec.scale, window=spec.window or None)
+    torch.cuda.synchronize()
+    _convex_hull_check(o, v, spec)
+    rows = _sample_rows(spec)
+    o_ref, lse_ref = oracle.attention_rows(data.q, data.k, data.v, rows, spec.scale, spec.causal,
+                                           window=spec.window or None)
+    o_all, lse_all = to_f64(o), to_f64(lse)
+    compare(o_all[rows[:, 0], rows[:, 1], rows[:, 2]], lse_all[rows[:, 0], rows[:, 1], rows[:, 2]],
+            o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"{spec.name} ({len(rows)} rows)")
+
+
+def test_decode_window_workload_full_compare():
+    spec = inputs.SWA_DECODE
+    say(f"fa_decode_window full-size workload {spec.name}")
+    data = inputs.decode_inputs(spec)
+    import torch
+    q = bf16_to_device(data.q)
+    kc, vc = bf16_to_device(data.k_cache), bf16_to_device(data.v_cache)
+    o, lse = api.decode(q, kc, vc, torch.from_numpy(data.seq_lens).cuda(), num_splits=spec.num_splits,
+                        scale=spec.scale, window=spec.window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale,
+                                   window=spec.window)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)

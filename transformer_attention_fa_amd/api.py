@@ -5,8 +5,9 @@ kernels behind the C ABI.  torch is used for device memory and for the
 current stream; there is no CPU or PyTorch fallback -- if libfa.so is missing
 or a call fails, an exception is raised.
 
-Entry points mirror the C names: ``fwd`` (fa_fwd, bf16), ``fwd_f32``
-(fa_fwd_f32), ``decode`` (fa_decode), ``decode_workspace_bytes``.
+Entry points mirror the C names: ``fwd`` (fa_fwd, bf16; with ``window=W``
+fa_fwd_window), ``fwd_f32`` (fa_fwd_f32), ``decode`` (fa_decode; with
+``window=W`` fa_decode_window), ``decode_workspace_bytes``.
 ``scale=None`` means 1/sqrt(d), like the ``softmax_scale=None`` default of the
 flash_attn_func usage shown in "Attention mechanism evolution: MHA -> MLA,
 Flash Attention" (toolsku.com), Flash Attention section.
@@ -21,8 +22,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_f32", "fa_decode", "fa_decode_workspace_bytes",
-            "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode", "fa_decode_window",
+            "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error")
 
 _lib = None
 
@@ -46,12 +47,16 @@ def load():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
+    lib.fa_fwd_window.restype = i
     lib.fa_fwd_f32.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd_f32.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode.restype = i
+    lib.fa_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
+    lib.fa_decode_window.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -96,7 +101,7 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def _fwd(fn, dtype, q, k, v, causal, scale, out, lse):
+def _fwd(fn, dtype, q, k, v, causal, scale, out, lse, mask_arg=None):
     torch = _torch()
     _require(q, "q", dtype, 4)
     _require(k, "k", dtype, 4, q.device)
@@ -122,17 +127,23 @@ def _fwd(fn, dtype, q, k, v, causal, scale, out, lse):
     lse_t = None if lse is False else lse
     with torch.cuda.device(q.device):
         check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), _ptr(lse_t),
-                 B, H, H_kv, N_q, N_k, d, float(scale), int(bool(causal)), _stream(q.device)))
+                 B, H, H_kv, N_q, N_k, d, float(scale),
+                 int(bool(causal)) if mask_arg is None else int(mask_arg), _stream(q.device)))
     return out, lse_t
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None, window=None):
     """fa_fwd: bf16 q [B,H,N_q,d], k/v [B,H_kv,N_k,d] -> (o bf16 [B,H,N_q,d], lse fp32 [B,H,N_q]).
 
-    Pass ``lse=False`` to skip the log-sum-exp output.
+    Pass ``lse=False`` to skip the log-sum-exp output.  ``window=W`` calls
+    fa_fwd_window (causal sliding window of W keys; ``causal`` must be true).
     """
     torch = _torch()
-    return _fwd(load().fa_fwd, torch.bfloat16, q, k, v, causal, scale, out, lse)
+    if window is None:
+        return _fwd(load().fa_fwd, torch.bfloat16, q, k, v, causal, scale, out, lse)
+    if not causal:
+        raise ValueError("a sliding window is causal: pass causal=True")
+    return _fwd(load().fa_fwd_window, torch.bfloat16, q, k, v, True, scale, out, lse, mask_arg=int(window))
 
 
 def fwd_f32(q, k, v, causal: bool = False, scale: float | None = None, out=None, lse=None):
@@ -146,11 +157,12 @@ def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
 
 
 def decode(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | None = None,
-           out=None, lse=None, workspace=None):
+           out=None, lse=None, workspace=None, window=None):
     """fa_decode: q [B,H,d], caches [B,H_kv,N_max,d] (bf16), seq_lens [B] int32 on the device.
 
     Returns (o bf16 [B,H,d], lse fp32 [B,H]).  ``workspace`` (uint8 tensor) may
-    be passed to avoid an allocation per call.
+    be passed to avoid an allocation per call.  ``window=W`` calls
+    fa_decode_window (the query sees the last W rows of its cache).
     """
     torch = _torch()
     _require(q, "q", torch.bfloat16, 3)
@@ -179,7 +191,13 @@ def decode(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | N
         _require(lse, "lse", torch.float32, 2, q.device)
     lse_t = None if lse is False else lse
     with torch.cuda.device(q.device):
-        check(load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
-                               out.data_ptr(), _ptr(lse_t), B, H, H_kv, N_max, d, float(scale),
-                               int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+        if window is None:
+            check(load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                   out.data_ptr(), _ptr(lse_t), B, H, H_kv, N_max, d, float(scale),
+                                   int(num_splits), workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+        else:
+            check(load().fa_decode_window(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+                                          seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t), B, H, H_kv, N_max, d,
+                                          float(scale), int(window), int(num_splits), workspace.data_ptr(),
+                                          workspace.numel(), _stream(q.device)))
     return out, lse_t

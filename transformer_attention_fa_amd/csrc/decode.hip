@@ -10,7 +10,9 @@
 // H/H_kv query heads).
 //
 // Split pass: workgroup (c, KV head and head group, b) takes keys
-// [c*L, min((c+1)*L, len)) with L = ceil(len / num_splits) and serves up to 16
+// [f + c*L, min(f + (c+1)*L, len)) with L = ceil((len - f) / num_splits), where
+// f = 0, or f = max(0, len - W) with a sliding window of W keys ("Attention
+// variants" §4: the newest token sees the W most recent rows), and serves up to 16
 // query heads that share one KV head, so each K/V byte of the chunk crosses HBM
 // once for all of them.  The chunk is cut into 16-key tiles dealt round robin
 // to the 4 waves; each wave streams its tiles into its own slice of LDS with
@@ -74,6 +76,7 @@ struct SplitParams {
     float* part_o;
     float* part_lse;
     int B, H, H_kv, N_max, S, rep, ngrp;
+    int window;   // keys seen: the last `window` rows of the cache, 0 = all
     float c;      // scale * log2(e), > 0
 };
 
@@ -177,6 +180,12 @@ __device__ __forceinline__ int clamped_len(const SplitParams& p, int b)
     return min(max(p.seq_lens[b], 0), p.N_max);   // never outside the cache
 }
 
+// keys read for a sequence of length len: all of them, or the last `window`
+__device__ __forceinline__ int key_start(const SplitParams& p, int len)
+{
+    return p.window > 0 ? max(0, len - p.window) : 0;
+}
+
 // Workgroups are dispatched in index order with blockIdx.z slowest, so z picks
 // the sequence by rank of length, longest first: the largest chunks start
 // first and the grid drains on the shortest ones.  Ranks order by length
@@ -186,10 +195,14 @@ __device__ __forceinline__ int sequence_for(const SplitParams& p, int z)
 {
     if (p.B > 64) return z;
     const int lane = threadIdx.x & 63;
-    const int mine = lane < p.B ? clamped_len(p, lane) : -1;
+    auto work = [&](int b) __attribute__((always_inline)) {   // keys the sequence reads
+        const int len = clamped_len(p, b);
+        return len - key_start(p, len);
+    };
+    const int mine = lane < p.B ? work(lane) : -1;
     int rank = 0;
     for (int j = 0; j < p.B; ++j) {
-        const int lj = clamped_len(p, j);
+        const int lj = work(j);
         rank += (lj > mine) || (lj == mine && j < lane);
     }
     const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < p.B && rank == z);
@@ -224,8 +237,9 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     const int l16 = lane & 15, g4 = lane >> 4;
 
     const int len = clamped_len(p, b);
-    const int L = (len + p.S - 1) / p.S;
-    const int j0 = c * L;
+    const int kfirst = key_start(p, len);
+    const int L = (len - kfirst + p.S - 1) / p.S;
+    const int j0 = kfirst + c * L;
     const int nkeys = max(0, min(j0 + L, len) - j0);
     const int ntiles = (nkeys + TK - 1) / TK;
     const int nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles w, w+4, ...
@@ -482,6 +496,7 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     p.H_kv = a.H_kv;
     p.N_max = a.N_max;
     p.S = a.num_splits;
+    p.window = a.window;
     p.rep = a.H / a.H_kv;
     p.ngrp = (p.rep + 15) / 16;               // groups of up to 16 query heads per KV head
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;

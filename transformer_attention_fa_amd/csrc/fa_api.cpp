@@ -62,6 +62,47 @@ fa_status_t from_hip(hipError_t e, const char* what)
     return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+size_t workspace_bytes_for(int B, int H, int d, int num_splits)
+{
+    if (B < 1 || H < 1 || d < 1 || num_splits < 1 || num_splits > 256) return 0;
+    if (too_large(B, H, num_splits, d + 1)) return 0;
+    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
+    size_t o_bytes = rows * (size_t)d * sizeof(float);
+    o_bytes = (o_bytes + 255) / 256 * 256;           // partial lse starts 256-byte aligned
+    return o_bytes + rows * sizeof(float);
+}
+
+fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cache,
+                          const int* seq_lens, void* o, float* lse,
+                          int B, int H, int H_kv, int N_max, int d, float scale,
+                          int num_splits, void* workspace, size_t workspace_bytes, int window,
+                          hipStream_t stream, const char* name)
+{
+    fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
+    if (s != FA_OK) return s;
+    if (!seq_lens)
+        return fail(FA_ERR_INVALID_ARGUMENT, "null seq_lens");
+    if (!aligned(seq_lens, 4))
+        return fail(FA_ERR_INVALID_ARGUMENT, "seq_lens must be 4-byte aligned");
+    if (num_splits < 1 || num_splits > 256)
+        return fail(FA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..256", num_splits);
+    if (!workspace || !aligned(workspace, 16))
+        return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 16-byte aligned");
+    size_t need = workspace_bytes_for(B, H, d, num_splits);
+    if (need == 0 || workspace_bytes < need)
+        return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
+                    workspace_bytes, need);
+    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
+    size_t o_bytes = (rows * (size_t)d * sizeof(float) + 255) / 256 * 256;
+    fa::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse,
+                     static_cast<float*>(workspace),
+                     reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes),
+                     B, H, H_kv, N_max, d, num_splits, scale, window};
+    char what[64];
+    snprintf(what, sizeof what, "%s launch", name);
+    return from_hip(fa::launch_decode(a, stream), what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,8 +126,20 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
 {
     fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
     if (s != FA_OK) return s;
-    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0, 0};
     return from_hip(fa::launch_fwd_bf16(a, stream), "fa_fwd launch");
+}
+
+fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int H, int H_kv, int N_q, int N_k, int d,
+                          float scale, int window, hipStream_t stream)
+{
+    fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
+    if (s != FA_OK) return s;
+    if (window < 1)
+        return fail(FA_ERR_INVALID_ARGUMENT, "window=%d must be at least 1", window);
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, 1, window};
+    return from_hip(fa::launch_fwd_bf16(a, stream), "fa_fwd_window launch");
 }
 
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -95,18 +148,13 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
 {
     fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
     if (s != FA_OK) return s;
-    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0};
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0, 0};
     return from_hip(fa::launch_fwd_f32(a, stream), "fa_fwd_f32 launch");
 }
 
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits)
 {
-    if (B < 1 || H < 1 || d < 1 || num_splits < 1 || num_splits > 256) return 0;
-    if (too_large(B, H, num_splits, d + 1)) return 0;
-    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
-    size_t o_bytes = rows * (size_t)d * sizeof(float);
-    o_bytes = (o_bytes + 255) / 256 * 256;           // partial lse starts 256-byte aligned
-    return o_bytes + rows * sizeof(float);
+    return workspace_bytes_for(B, H, d, num_splits);
 }
 
 fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -115,27 +163,20 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       int num_splits, void* workspace, size_t workspace_bytes,
                       hipStream_t stream)
 {
-    fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
-    if (s != FA_OK) return s;
-    if (!seq_lens)
-        return fail(FA_ERR_INVALID_ARGUMENT, "null seq_lens");
-    if (!aligned(seq_lens, 4))
-        return fail(FA_ERR_INVALID_ARGUMENT, "seq_lens must be 4-byte aligned");
-    if (num_splits < 1 || num_splits > 256)
-        return fail(FA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..256", num_splits);
-    if (!workspace || !aligned(workspace, 16))
-        return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 16-byte aligned");
-    size_t need = fa_decode_workspace_bytes(B, H, d, num_splits);
-    if (need == 0 || workspace_bytes < need)
-        return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
-                    workspace_bytes, need);
-    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
-    size_t o_bytes = (rows * (size_t)d * sizeof(float) + 255) / 256 * 256;
-    fa::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse,
-                     static_cast<float*>(workspace),
-                     reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes),
-                     B, H, H_kv, N_max, d, num_splits, scale};
-    return from_hip(fa::launch_decode(a, stream), "fa_decode launch");
+    return decode_common(q, k_cache, v_cache, seq_lens, o, lse, B, H, H_kv, N_max, d, scale, num_splits,
+                         workspace, workspace_bytes, 0, stream, "fa_decode");
+}
+
+fa_status_t fa_decode_window(const void* q, const void* k_cache, const void* v_cache,
+                             const int* seq_lens, void* o, float* lse,
+                             int B, int H, int H_kv, int N_max, int d, float scale,
+                             int window, int num_splits, void* workspace, size_t workspace_bytes,
+                             hipStream_t stream)
+{
+    if (window < 1)
+        return fail(FA_ERR_INVALID_ARGUMENT, "window=%d must be at least 1", window);
+    return decode_common(q, k_cache, v_cache, seq_lens, o, lse, B, H, H_kv, N_max, d, scale, num_splits,
+                         workspace, workspace_bytes, window, stream, "fa_decode_window");
 }
 
 }  // extern "C"

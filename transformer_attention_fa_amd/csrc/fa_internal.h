@@ -18,6 +18,7 @@ struct FwdArgs {
     int B, H, H_kv, N_q, N_k, d;
     float scale;         // softmax scale on q.k
     int causal;
+    int window;          // sliding window in keys (causal only), 0 = none
 };
 
 // One decode step, as validated by fa_decode.
@@ -32,6 +33,7 @@ struct DecodeArgs {
     float* part_lse;     // [B,H,S]    workspace
     int B, H, H_kv, N_max, d, num_splits;
     float scale;
+    int window;          // the query sees the last `window` rows, 0 = all
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

@@ -88,6 +88,7 @@ struct Params {
     int B, H, H_kv, N_q, N_k;
     int rep;      // H / H_kv
     int nqb;      // query blocks per head
+    int window;   // sliding window in keys (causal only); 0 = none
     int group;    // heads per longest-first group of the workgroup order
     float c;      // scale * log2(e), > 0
 };
@@ -194,9 +195,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     if (CAUSAL) kend = min(p.N_k, q0 + BM + off);
     const int nkb = kend > 0 ? (kend + BN - 1) / BN : 0;
     const int last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
-    // tiles this wave computes: 0 .. nkb_w-1 (later ones lie after its last row)
+    // tiles this wave computes: a_w .. nkb_w-1.  Later tiles lie after its last
+    // row; with a sliding window ("Attention variants" §4: each row sees the W
+    // keys ending at its last causally visible key) earlier tiles lie before
+    // the window of its first row.
     int nkb_w = nkb;
     if (CAUSAL) nkb_w = max(0, min(nkb, (qw0 + 31 + off) / BN + 1));
+    int kb_lo = 0, a_w = 0;
+    const bool windowed = CAUSAL && p.window > 0;
+    const int first_vis = windowed ? qi + off - p.window + 1 : 0;   // first visible key of this lane's row
+    if (windowed) {
+        kb_lo = min(nkb, max(0, q0 + off - p.window + 1) / BN);
+        a_w = min(nkb_w, max(0, qw0 + off - p.window + 1) / BN);
+    }
 
     // ---- tile loads: chunk position -> (row, global chunk)
     int ld_voff[LOADS];
@@ -341,6 +352,15 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 for (int r = 0; r < 16; ++r)
                     if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][r] = kNegInf;
         }
+        // keys before the window of some row of this wave
+        if (windowed && key0 < qw0 + 31 + off - p.window + 1) {
+            const int lo = first_vis - key0 - 4 * half;
+#pragma unroll
+            for (int kt = 0; kt < NT; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (kt * 32 + 8 * (r >> 2) + (r & 3) < lo) s[kt][r] = kNegInf;
+        }
         // row max of the tile; the running max is raised only when it grows by
         // more than the slack (then O and l are rescaled)
         float mx = kNegInf;
@@ -389,17 +409,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- periods j = 0 .. nkb.  In period j every wave reads K tile j and V
-    //      tile j-1 only, while K tile j+1 and V tile j load into the other
+    // ---- periods j = kb_lo .. nkb.  In period j every wave reads K tile j and
+    //      V tile j-1 only, while K tile j+1 and V tile j load into the other
     //      slots (K tile j in K slot j%2, V tile j in V slot j%2).  The two
     //      waves that share a SIMD run the two phases in opposite order, so one
     //      wave's softmax overlaps the other's matrix-core work:
     //        waves 0-3:  MFMA(PV j-1, S j), softmax(j)
     //        waves 4-7:  softmax(j-1), MFMA(PV j-1, S j)
-    //      A wave computes tiles 0 .. nkb_w-1: period 0 has no PV, period
-    //      nkb_w no S, and later periods only keep the barriers and loads.
-    //      Each role has its own loop (straight-line phases keep the register
-    //      allocation tight); both pass the same nkb+1 barriers.
+    //      A wave computes tiles a_w .. nkb_w-1: period a_w has no PV, period
+    //      nkb_w no S, and the periods outside only keep the barriers and
+    //      loads.  Each role has its own loop (straight-line phases keep the
+    //      register allocation tight); all waves pass the same barriers.
     // One period: the barrier, this period's tile loads into the free slots,
     // then the role's phases (SM: 1 = softmax of tile j-1 before the MFMAs,
     // 2 = softmax of tile j after them).  The slot pointers are restrict
@@ -437,16 +457,17 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     using CNPV = std::integral_constant<int, NPV>;
     using CNSTEP = std::integral_constant<int, NSTEP>;
 
-    if (nkb > 0) issue(kbase, 0, lds);
-    int j = 0;
-    if (nkb_w > 0) {
+    if (nkb > kb_lo) issue(kbase, kb_lo, lds + (kb_lo & 1) * TILE);
+    int j = kb_lo;
+    for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{});    // tiles before this wave's window
+    if (nkb_w > a_w) {
         if (role == 0) {
-            run_period(0, CNPV{}, CNSTEP{}, C2{});
-            for (j = 1; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{});
+            run_period(j, CNPV{}, CNSTEP{}, C2{});
+            for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{});
             run_period(j, C0{}, CNPV{}, C0{});            // j == nkb_w: PV of the last tile
         } else {
-            run_period(0, CNPV{}, CNSTEP{}, C0{});
-            for (j = 1; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{});
+            run_period(j, CNPV{}, CNSTEP{}, C0{});
+            for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{});
             run_period(j, C0{}, CNPV{}, C1{});
         }
         ++j;
@@ -495,6 +516,7 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     p.rep = a.H / a.H_kv;
     p.nqb = (a.N_q + BM - 1) / BM;
     p.group = group < 1 ? 1 : group;
+    p.window = CAUSAL ? a.window : 0;
     // scale 0 runs as a tiny positive scale: every exp2 argument then rounds to
     // 0 exactly as with scale 0, and masked scores stay -inf instead of NaN
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;

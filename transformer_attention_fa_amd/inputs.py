@@ -97,15 +97,31 @@ class Prefill:
     dtype: str            # "bf16" or "f32"
     seed: int
     k_scale: float = 1.0  # every K element multiplied by this (exact power of two)
+    window: int = 0       # sliding window in keys (causal only); 0 = none
 
     @property
     def scale(self) -> float:
         return 1.0 / math.sqrt(self.d)
 
     def flops(self) -> float:
-        """Algorithmic FLOPs: 4*B*H*N_q*N_k*d, halved when causal."""
+        """Algorithmic FLOPs: 4*B*H*N_q*N_k*d, halved when causal (square
+        problems); 4*B*H*d*(visible query-key pairs) with a sliding window or a
+        non-square causal problem."""
+        if self.window or (self.causal and self.N_q != self.N_k):
+            return 4.0 * self.B * self.H * self.d * visible_pairs(self.N_q, self.N_k, self.causal, self.window)
         f = 4.0 * self.B * self.H * self.N_q * self.N_k * self.d
         return f / 2 if self.causal else f
+
+
+def visible_pairs(n_q: int, n_k: int, causal: bool, window: int = 0) -> int:
+    """Number of (query, key) pairs the mask lets through: row i sees keys up to
+    i + (n_k - n_q) when causal, and only the last `window` of them with a window."""
+    if not causal:
+        return n_q * n_k
+    i = np.arange(n_q, dtype=np.int64)
+    hi = np.minimum(n_k, i + (n_k - n_q) + 1)
+    lo = np.maximum(0, i + (n_k - n_q) - window + 1) if window else np.zeros_like(i)
+    return int(np.maximum(0, hi - lo).sum())
 
 
 @dataclass(frozen=True)
@@ -121,6 +137,7 @@ class Decode:
     num_splits: int
     seed: int
     dtype: str = "bf16"
+    window: int = 0       # the query sees the last `window` cached rows; 0 = all
 
     @property
     def scale(self) -> float:
@@ -136,6 +153,15 @@ GQA_PREFILL = Prefill("gqa_prefill_b1_h32_hkv8_n8192_d128_causal_k2", 1, 32, 8, 
                       "bf16", 3, k_scale=2.0)
 MQA_PREFILL = Prefill("mqa_prefill_b4_h64_hkv1_n4096_d128", 4, 64, 1, 4096, 4096, 128, False, "bf16", 4)
 GQA_DECODE = Decode("gqa_decode_b32_h32_hkv8_d128_len8k_32k_s16", 32, 32, 8, 128, 8192, 32768, 32768, 16, 5)
+
+# Next steps on the same path ("Attention variants" §4 sliding window, with the
+# window of Mistral-class models; a prompt chunk appended after a cache, the
+# bottom-right causal case of "Attention mechanism evolution" KV-cache code).
+SWA_PREFILL = Prefill("swa_prefill_b1_h32_hkv8_n16384_w4096_d128", 1, 32, 8, 16384, 16384, 128, True, "bf16", 6,
+                      window=4096)
+SWA_DECODE = Decode("swa_decode_b32_h32_hkv8_d128_len8k_32k_w4096_s8", 32, 32, 8, 128, 8192, 32768, 32768, 8, 5,
+                    window=4096)
+CHUNKED_PREFILL = Prefill("chunked_prefill_b4_h32_hkv8_q512_k8192_d128", 4, 32, 8, 512, 8192, 128, True, "bf16", 7)
 
 PREFILL_WORKLOADS = (SINGLE_HEAD_F32, SINGLE_HEAD_F32_CAUSAL, MHA_PREFILL, GQA_PREFILL, MQA_PREFILL)
 
