@@ -35,6 +35,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="mha", choices=["mha", "gqa", "mqa"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-next", action="store_true",
+                    help="skip the sliding-window and chunked-prefill measurements (the 'next' object)")
     ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
                     help="time one half of the step only (for profiling runs); 'copy' runs a plain "
                          "1 GiB device-to-device copy, the reference for scaling HBM byte counters")
@@ -80,6 +82,63 @@ def cpu_baseline(spec, n_batches):
             "sample": (f"the whole {spec.name} workload" if n_batches == spec.B else
                        f"{n_batches} of {spec.B} sequences ({n_batches * spec.H} heads) of {spec.name}")
                       + f", fp64, {dt:.2f} s wall"}
+
+
+def time_launches(fn, steps, warmup):
+    """Average / median / min of `steps` launches (HIP events on the current stream), in ms."""
+    import numpy as np
+    import torch
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return float(t.mean()), float(np.median(t)), float(t.min())
+
+
+def measure_next(dev_bf16, steps, warmup, decode_state=None):
+    """The sliding-window and chunked-prefill rows, each on its own workload."""
+    import torch
+    from transformer_attention_fa_amd import api, inputs, roofline
+    out = {}
+    for spec in (inputs.SWA_PREFILL, inputs.CHUNKED_PREFILL):
+        data = inputs.prefill_inputs(spec)
+        q, k, v = (dev_bf16(x) for x in (data.q, data.k, data.v))
+        del data
+        o = torch.empty_like(q)
+        lse = torch.empty((spec.B, spec.H, spec.N_q), dtype=torch.float32, device=q.device)
+        win = spec.window or None
+        avg, med, mn = time_launches(lambda: api.fwd(q, k, v, causal=spec.causal, scale=spec.scale, out=o, lse=lse,
+                                                     window=win), steps, warmup)
+        flops = spec.flops()
+        tf = flops / (avg * 1e-3) / 1e12
+        out[spec.name] = {"entry": "fa_fwd_window" if win else "fa_fwd", "value": tf, "unit": "TFLOP/s",
+                          "frac_mfma_peak": tf / roofline.PEAK_BF16_TFLOPS, "ms_avg": avg, "ms_median": med,
+                          "ms_min": mn, "flop_per_launch": flops, "window": spec.window,
+                          "shape": {"B": spec.B, "H": spec.H, "H_kv": spec.H_kv, "N_q": spec.N_q, "N_k": spec.N_k,
+                                    "d": spec.d, "causal": spec.causal}}
+        del q, k, v, o, lse
+    if decode_state is not None:
+        spec = inputs.SWA_DECODE
+        dq, kc, vc, lens, seq_lens, base = decode_state
+        assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
+        ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
+                         device=dq.device)
+        d_o = torch.empty_like(dq)
+        d_lse = torch.empty((spec.B, spec.H), dtype=torch.float32, device=dq.device)
+        avg, med, mn = time_launches(lambda: api.decode(dq, kc, vc, lens, num_splits=spec.num_splits,
+                                                        scale=spec.scale, out=d_o, lse=d_lse, workspace=ws,
+                                                        window=spec.window), steps, warmup)
+        kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, [min(int(n), spec.window) for n in seq_lens])
+        gbps = kv / (avg * 1e-3) / 1e9
+        out[spec.name] = {"entry": "fa_decode_window", "value": gbps, "unit": "GB/s",
+                          "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS, "ms_avg": avg, "ms_median": med,
+                          "ms_min": mn, "kv_bytes": kv, "window": spec.window, "num_splits": spec.num_splits}
+    return out
 
 
 def main():
@@ -194,6 +253,9 @@ def main():
         if not do_prefill:
             rec.update({"value": gbps, "unit": "GB/s"})
     rec["config"] = config
+    if args.only is None and not args.no_next:
+        rec["next"] = measure_next(dev_bf16, args.steps, args.warmup,
+                                   (dq, kc, vc, lens, seq_lens, dspec) if do_decode else None)
     if do_prefill and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pspec, n_batches=pspec.B)
     props = torch.cuda.get_device_properties(dev)
