@@ -152,3 +152,32 @@ def decode(q, k_cache, v_cache, seq_lens, scale: float, window=None):
     if rc != 0:
         raise ValueError(f"oracle_decode failed with code {rc}")
     return o, lse
+
+
+def gather_pages(pages, block_table, seq_lens):
+    """Contiguous cache [B,H_kv,N,d] from a paged pool [P,H_kv,page_size,d].
+
+    Logical row r of sequence b is row r % page_size of physical page
+    block_table[b, r // page_size] ("Attention variants" §5: the KV cache is
+    cut into fixed-size blocks managed like virtual-memory pages).  Rows at or
+    past seq_lens[b] are left as NaN and never read by decode().
+    """
+    pages = np.asarray(pages)
+    bt = np.asarray(block_table)
+    lens = np.asarray(seq_lens)
+    P, H_kv, ps, d = pages.shape
+    B = bt.shape[0]
+    n = int(bt.shape[1]) * ps
+    fill = np.uint16(0x7FC0) if pages.dtype == np.uint16 else np.nan
+    out = np.full((B, H_kv, n, d), fill, dtype=pages.dtype)
+    for b in range(B):
+        r = np.arange(int(lens[b]))
+        out[b, :, :len(r)] = pages[bt[b, r // ps], :, r % ps].transpose(1, 0, 2)
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float):
+    """decode() on a paged cache: gather each sequence's rows, then decode."""
+    k = gather_pages(k_pages, block_table, seq_lens)
+    v = gather_pages(v_pages, block_table, seq_lens)
+    return decode(q, k, v, seq_lens, scale)

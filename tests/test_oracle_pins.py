@@ -527,3 +527,52 @@ def test_decode_window():
             o1, l1 = oracle.attention(q[b:b + 1, :, None, :], k[b:b + 1, :, :L], v[b:b + 1, :, :L], 0.5, True, window=w)
             np.testing.assert_allclose(o[b], o1[0, :, 0], atol=TOL, rtol=0)
             np.testing.assert_allclose(lse[b], l1[0, :, 0], atol=TOL, rtol=0)
+
+
+# --------------------------------------------------------------------------
+# P-k: paged KV cache ("Attention variants" §5: the cache cut into fixed-size
+# blocks managed like virtual-memory pages).  Reading the pages through the
+# block table must give back exactly the contiguous cache.
+# --------------------------------------------------------------------------
+def _to_pages(cache, lens, ps, order):
+    """Cut a contiguous cache [B,H_kv,N,d] into pages placed at `order` positions of a pool."""
+    B, H_kv, N, d = cache.shape
+    nb = (N + ps - 1) // ps
+    pool = np.full((len(order) + 3, H_kv, ps, d), np.nan)      # spare pages stay NaN
+    table = np.zeros((B, nb), np.int32)
+    it = iter(order)
+    for b in range(B):
+        for blk in range((int(lens[b]) + ps - 1) // ps):
+            page = next(it)
+            table[b, blk] = page
+            rows = cache[b, :, blk * ps:min((blk + 1) * ps, int(lens[b]))]
+            pool[page, :, :rows.shape[1]] = rows
+    return pool, table
+
+
+def test_gather_pages_by_hand():
+    # two sequences, page_size 2: sequence 0 owns pages 3 and 0, sequence 1 owns page 2
+    pool = np.arange(4 * 1 * 2 * 1, dtype=np.float64).reshape(4, 1, 2, 1)   # page p holds rows [2p, 2p+1]
+    table = np.array([[3, 0], [2, 1]], np.int32)
+    out = oracle.gather_pages(pool, table, np.array([3, 2], np.int32))
+    assert list(out[0, 0, :3, 0]) == [6.0, 7.0, 0.0]
+    assert list(out[1, 0, :2, 0]) == [4.0, 5.0]
+    assert np.isnan(out[0, 0, 3, 0]) and np.all(np.isnan(out[1, 0, 2:, 0]))
+
+
+@pytest.mark.parametrize("ps", [1, 2, 16])
+def test_paged_decode_equals_contiguous(ps):
+    B, H, H_kv, N, d = 3, 4, 2, 37, 8
+    rng = np.random.default_rng(141)
+    k = rng.standard_normal((B, H_kv, N, d))
+    v = rng.standard_normal((B, H_kv, N, d))
+    lens = np.array([1, 20, 37], np.int32)
+    q = rng.standard_normal((B, H, d))
+    o_ref, l_ref = oracle.decode(q, k, v, lens, 0.4)
+    n_pages = sum((int(n) + ps - 1) // ps for n in lens)
+    for order in (np.arange(n_pages), rng.permutation(n_pages + 3)[:n_pages]):
+        pool, table = _to_pages(k, lens, ps, order)
+        vpool, _ = _to_pages(v, lens, ps, order)
+        o, l = oracle.decode_paged(q, pool, vpool, table, lens, 0.4)
+        np.testing.assert_array_equal(o, o_ref)
+        np.testing.assert_array_equal(l, l_ref)
