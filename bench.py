@@ -101,7 +101,8 @@ def time_launches(fn, steps, warmup):
 
 
 def measure_next(dev_bf16, steps, warmup, decode_state=None):
-    """The sliding-window and chunked-prefill rows, each on its own workload."""
+    """The sliding-window, chunked-prefill and paged-cache rows, each on its own workload."""
+    import numpy as np
     import torch
     from transformer_attention_fa_amd import api, inputs, roofline
     out = {}
@@ -138,6 +139,35 @@ def measure_next(dev_bf16, steps, warmup, decode_state=None):
         out[spec.name] = {"entry": "fa_decode_window", "value": gbps, "unit": "GB/s",
                           "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS, "ms_avg": avg, "ms_median": med,
                           "ms_min": mn, "kv_bytes": kv, "window": spec.window, "num_splits": spec.num_splits}
+        # paged cache: the same rows dealt onto shuffled 16-row pages of a pool
+        spec = inputs.PAGED_DECODE
+        assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
+        table, num_pages = inputs.page_table(seq_lens, spec.page_size, spec.seed)
+        ps = spec.page_size
+        b_idx = np.concatenate([np.full(int(n), b) for b, n in enumerate(seq_lens)])
+        r_idx = np.concatenate([np.arange(int(n)) for n in seq_lens])
+        page_idx = torch.from_numpy(table[b_idx, r_idx // ps].astype(np.int64)).to(dq.device)
+        slot_idx = torch.from_numpy(r_idx % ps).to(dq.device)
+        bi, ri = torch.from_numpy(b_idx).to(dq.device), torch.from_numpy(r_idx).to(dq.device)
+        pools = []
+        for cache in (kc, vc):
+            pool = torch.zeros((num_pages, spec.H_kv, ps, spec.d), dtype=cache.dtype, device=dq.device)
+            pool[page_idx, :, slot_idx] = cache[bi, :, ri]
+            pools.append(pool)
+        del page_idx, slot_idx, bi, ri
+        bt = torch.from_numpy(np.maximum(table, 0)).to(dq.device)
+        ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
+                         device=dq.device)
+        avg, med, mn = time_launches(lambda: api.decode_paged(dq, pools[0], pools[1], bt, lens,
+                                                              num_splits=spec.num_splits, scale=spec.scale, out=d_o,
+                                                              lse=d_lse, workspace=ws), steps, warmup)
+        kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, seq_lens)
+        gbps = kv / (avg * 1e-3) / 1e9
+        out[spec.name] = {"entry": "fa_decode_paged", "value": gbps, "unit": "GB/s",
+                          "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS, "ms_avg": avg, "ms_median": med,
+                          "ms_min": mn, "kv_bytes": kv, "page_size": ps, "num_pages": num_pages,
+                          "num_splits": spec.num_splits}
+        del pools
     return out
 
 

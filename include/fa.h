@@ -16,6 +16,8 @@
  *          rep = H/G, repeat_interleave on the head axis, scores / sqrt(d_k)),
  *       §3 FlashAttention tiling and online softmax (exact, not approximate),
  *       §4 sliding-window attention (each token sees the W most recent tokens),
+ *       §5 serving memory: paged KV cache (fixed-size blocks managed like
+ *          virtual-memory pages), KV quantisation,
  *       §5.5 causal block skip, §7 decode is memory-bandwidth bound,
  *       troubleshooting list: H must be a multiple of G.
  *  [ME] "Attention mechanism evolution: MHA -> MLA, Flash Attention" (toolsku.com)
@@ -164,6 +166,32 @@ fa_status_t fa_decode_window(const void* q, const void* k_cache, const void* v_c
                              int B, int H, int H_kv, int N_max, int d, float scale,
                              int window, int num_splits, void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/*
+ * fa_decode_paged -- fa_decode on a paged KV cache [AV §5: the cache is cut
+ * into fixed-size blocks managed like virtual-memory pages, so sequences need
+ * no contiguous allocation].  Row r of sequence b, KV head g lives at
+ *   k_pages[block_table[b * max_blocks + r / page_size], g, r % page_size, :]
+ * and likewise in v_pages.  Results equal fa_decode on the gathered cache up
+ * to rounding order.
+ *   k_pages, v_pages [num_pages, H_kv, page_size, d] bf16, device (the pools)
+ *   block_table [B, max_blocks] int32, device: physical page of each logical
+ *               block; entries are trusted device data -- the kernel clamps
+ *               each one into 0..num_pages-1, so a bad entry can never read
+ *               outside the pools; only blocks holding rows < seq_lens[b] are read
+ *   seq_lens    [B] int32, device; clamped into 0..max_blocks*page_size
+ *   page_size   rows per page, a multiple of 16 (others: FA_ERR_UNSUPPORTED)
+ *   max_blocks, num_pages >= 1
+ *   The keys of each sequence are cut into num_splits chunks of
+ *   16 * ceil(ceil(seq_lens[b] / num_splits) / 16) rows (chunk edges on
+ *   16-row boundaries, so a tile never crosses a page).
+ *   Other arguments, workspace (same size as fa_decode) and errors as fa_decode.
+ */
+fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int* block_table, int max_blocks, const int* seq_lens,
+                            void* o, float* lse, int B, int H, int H_kv, int num_pages, int page_size,
+                            int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* Static text for a status code. */
 const char* fa_status_string(fa_status_t s);

@@ -141,3 +141,32 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(api, "LIB_PATH", str(tmp_path / "missing" / "libfa.so"))
     with pytest.raises(FileNotFoundError):
         api.load()
+
+
+GOOD_PAGED = dict(q=P, kp=P, vp=P, bt=P, max_blocks=8, lens=P, o=P, lse=P, B=4, H=8, H_kv=2, num_pages=64,
+                  page_size=32, d=128, scale=0.1, S=16, ws=P, ws_bytes=1 << 20)
+
+PAGED_CASES = [
+    ("null_block_table", dict(bt=None), INVALID),
+    ("block_table_misaligned", dict(bt=P + 2), INVALID),
+    ("max_blocks_zero", dict(max_blocks=0), INVALID),
+    ("num_pages_zero", dict(num_pages=0), INVALID),
+    ("page_size_zero", dict(page_size=0), INVALID),
+    ("page_size_24", dict(page_size=24), UNSUPPORTED),
+    ("null_seq_lens", dict(lens=None), INVALID),
+    ("splits_zero", dict(S=0), INVALID),
+    ("workspace_small", dict(ws_bytes=1000), INVALID),
+    ("H_not_multiple", dict(H=8, H_kv=3), INVALID),
+    ("d_unsupported", dict(d=80), UNSUPPORTED),
+    ("null_pool", dict(kp=None), INVALID),
+]
+
+
+@pytest.mark.parametrize("name,change,expect", PAGED_CASES, ids=[c[0] for c in PAGED_CASES])
+def test_decode_paged_rejects_before_launch(lib, name, change, expect):
+    a = dict(GOOD_PAGED, **change)
+    st = lib.fa_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["max_blocks"], a["lens"], a["o"], a["lse"],
+                             a["B"], a["H"], a["H_kv"], a["num_pages"], a["page_size"], a["d"], a["scale"], a["S"],
+                             a["ws"], a["ws_bytes"], None)
+    assert st == expect, (name, st, lib.fa_last_error())
+    assert lib.fa_last_error()

@@ -347,3 +347,76 @@ def test_decode_window_workload_full_compare():
     o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale,
                                    window=spec.window)
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+# ------------------------------------------------------------------ paged KV cache
+def _paged(data, page_size, seed):
+    table, num_pages = inputs.page_table(data.seq_lens, page_size, seed)
+    kp = inputs.to_pages(data.k_cache, data.seq_lens, table, num_pages, page_size, inputs.BF16_QNAN)
+    vp = inputs.to_pages(data.v_cache, data.seq_lens, table, num_pages, page_size, inputs.BF16_QNAN)
+    return kp, vp, table
+
+
+@pytest.mark.parametrize("page_size", [16, 32, 64, 256])
+@pytest.mark.parametrize("num_splits", [1, 7, 16])
+def test_decode_paged(page_size, num_splits):
+    import torch
+    spec = _small_decode_spec(H=8, H_kv=2, d=128, N_max=3000, B=6, seed=37)
+    lens = np.array([1, 2, 15, 16, 17, 3000], np.int32)
+    data = inputs.decode_inputs(spec, seq_lens=lens)
+    kp, vp, table = _paged(data, page_size, 41)
+    q = bf16_to_device(data.q)
+    o, lse = api.decode_paged(q, bf16_to_device(kp), bf16_to_device(vp), torch.from_numpy(table).cuda(),
+                              torch.from_numpy(lens).cuda(), num_splits=num_splits, scale=spec.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged(data.q, kp, vp, np.maximum(table, 0), lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL,
+            label=f"page {page_size} S={num_splits}")
+
+
+def test_decode_paged_d64_mqa():
+    import torch
+    spec = _small_decode_spec(H=16, H_kv=1, d=64, N_max=900, B=3, seed=43)
+    data = inputs.decode_inputs(spec)
+    kp, vp, table = _paged(data, 32, 47)
+    o, lse = api.decode_paged(bf16_to_device(data.q), bf16_to_device(kp), bf16_to_device(vp),
+                              torch.from_numpy(table).cuda(), torch.from_numpy(data.seq_lens).cuda(), num_splits=8,
+                              scale=spec.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label="paged d64")
+
+
+def test_decode_paged_clamps_bad_table_entries():
+    """Entries past the used blocks are never read; a bad entry of a used block
+    is clamped into the pool (so the result is that of the clamped table)."""
+    import torch
+    spec = _small_decode_spec(H=8, H_kv=2, d=128, N_max=500, B=3, seed=53)
+    lens = np.array([100, 260, 500], np.int32)
+    data = inputs.decode_inputs(spec, seq_lens=lens)
+    kp, vp, table = _paged(data, 64, 59)
+    bad = table.copy()
+    bad[0, 2:] = 1 << 30                  # blocks past 100 rows: never read
+    bad[1, 5] = -7                        # 260 rows use blocks 0..4: block 5 is never read
+    bad[2, 3] = 1 << 30                   # used: clamped to the last page
+    o, lse = api.decode_paged(bf16_to_device(data.q), bf16_to_device(kp), bf16_to_device(vp),
+                              torch.from_numpy(bad).cuda(), torch.from_numpy(lens).cuda(), num_splits=4,
+                              scale=spec.scale)
+    torch.cuda.synchronize()
+    clamped = np.clip(bad, 0, kp.shape[0] - 1)
+    o_ref, lse_ref = oracle.decode_paged(data.q, kp, vp, clamped, lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label="clamped table")
+
+
+def test_decode_paged_workload_full_compare():
+    import torch
+    spec = inputs.PAGED_DECODE
+    say(f"fa_decode_paged full-size workload {spec.name}")
+    data = inputs.decode_inputs(spec)
+    kp, vp, table = _paged(data, spec.page_size, spec.seed)
+    o, lse = api.decode_paged(bf16_to_device(data.q), bf16_to_device(kp), bf16_to_device(vp),
+                              torch.from_numpy(table).cuda(), torch.from_numpy(data.seq_lens).cuda(),
+                              num_splits=spec.num_splits, scale=spec.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)

@@ -7,7 +7,8 @@ or a call fails, an exception is raised.
 
 Entry points mirror the C names: ``fwd`` (fa_fwd, bf16; with ``window=W``
 fa_fwd_window), ``fwd_f32`` (fa_fwd_f32), ``decode`` (fa_decode; with
-``window=W`` fa_decode_window), ``decode_workspace_bytes``.
+``window=W`` fa_decode_window), ``decode_paged`` (fa_decode_paged),
+``decode_workspace_bytes``.
 ``scale=None`` means 1/sqrt(d), like the ``softmax_scale=None`` default of the
 flash_attn_func usage shown in "Attention mechanism evolution: MHA -> MLA,
 Flash Attention" (toolsku.com), Flash Attention section.
@@ -22,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode", "fa_decode_window",
+EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode", "fa_decode_window", "fa_decode_paged",
             "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error")
 
 _lib = None
@@ -57,6 +58,8 @@ def load():
     lib.fa_decode.restype = i
     lib.fa_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_decode_window.restype = i
+    lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode_paged.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -200,4 +203,42 @@ def decode(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | N
                                           seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t), B, H, H_kv, N_max, d,
                                           float(scale), int(window), int(num_splits), workspace.data_ptr(),
                                           workspace.numel(), _stream(q.device)))
+    return out, lse_t
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits: int = 16, scale: float | None = None,
+                 out=None, lse=None, workspace=None):
+    """fa_decode_paged: q [B,H,d]; page pools [num_pages,H_kv,page_size,d] (bf16);
+    block_table [B,max_blocks] and seq_lens [B] int32 on the device."""
+    torch = _torch()
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_pages, "k_pages", torch.bfloat16, 4, q.device)
+    _require(v_pages, "v_pages", torch.bfloat16, 4, q.device)
+    _require(block_table, "block_table", torch.int32, 2, q.device)
+    _require(seq_lens, "seq_lens", torch.int32, 1, q.device)
+    B, H, d = q.shape
+    num_pages, H_kv, page_size, dk = k_pages.shape
+    if dk != d or tuple(v_pages.shape) != tuple(k_pages.shape) or block_table.shape[0] != B or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, page pools, block_table and seq_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, 3, q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    elif lse is not False:
+        _require(lse, "lse", torch.float32, 2, q.device)
+    lse_t = None if lse is False else lse
+    with torch.cuda.device(q.device):
+        check(load().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
+                                     block_table.shape[1], seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t),
+                                     B, H, H_kv, num_pages, page_size, d, float(scale), int(num_splits),
+                                     workspace.data_ptr(), workspace.numel(), _stream(q.device)))
     return out, lse_t

@@ -77,6 +77,10 @@ struct SplitParams {
     float* part_lse;
     int B, H, H_kv, N_max, S, rep, ngrp;
     int window;   // keys seen: the last `window` rows of the cache, 0 = all
+    // paged cache: k and v are page pools [num_pages, H_kv, page_size, D];
+    // row r of sequence b is row r % page_size of page block_table[b, r / page_size]
+    const int* block_table;
+    int max_blocks, page_size, num_pages;
     float c;      // scale * log2(e), > 0
 };
 
@@ -209,7 +213,7 @@ __device__ __forceinline__ int sequence_for(const SplitParams& p, int z)
     return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
 }
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
 {
     constexpr int NW = 4;
@@ -238,13 +242,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
 
     const int len = clamped_len(p, b);
     const int kfirst = key_start(p, len);
-    const int L = (len - kfirst + p.S - 1) / p.S;
+    int L = (len - kfirst + p.S - 1) / p.S;
+    if (PAGED) L = (L + TK - 1) / TK * TK;   // chunks and tiles start on page-aligned rows
     const int j0 = kfirst + c * L;
     const int nkeys = max(0, min(j0 + L, len) - j0);
     const int ntiles = (nkeys + TK - 1) / TK;
     const int nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles w, w+4, ...
 
-    const size_t kv_row0 = ((size_t)b * p.H_kv + g) * (size_t)p.N_max + (size_t)j0;
+    const size_t kv_row0 = PAGED ? 0 : ((size_t)b * p.H_kv + g) * (size_t)p.N_max + (size_t)j0;
     const char* kbase = reinterpret_cast<const char*>(p.k + kv_row0 * D);
     const char* vbase = reinterpret_cast<const char*>(p.v + kv_row0 * D);
     char* wl = lds + w * WAVE_LDS;
@@ -260,8 +265,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     auto issue = [&](int t, int s) __attribute__((always_inline)) {
         const int key0 = t * TK;
         const unsigned bytes = (unsigned)min(TK, nkeys - key0) * ROWB;
-        const i32x4 rk = make_rsrc(kbase + (size_t)key0 * ROWB, bytes);
-        const i32x4 rv = make_rsrc(vbase + (size_t)key0 * ROWB, bytes);
+        size_t off = (size_t)key0 * ROWB;
+        if constexpr (PAGED) {
+            // the tile's 16 rows lie in one page (page_size % 16 == 0, aligned chunks)
+            const int row = j0 + key0;
+            const int blk = row / p.page_size;
+            int page = p.block_table[(size_t)b * p.max_blocks + blk];
+            page = min(max(page, 0), p.num_pages - 1);           // never outside the pool
+            off = (((size_t)page * p.H_kv + g) * p.page_size + (row - blk * p.page_size)) * ROWB;
+        }
+        const i32x4 rk = make_rsrc(kbase + off, bytes);
+        const i32x4 rv = make_rsrc(vbase + off, bytes);
         char* dst = wl + s * 2 * TILEB;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
@@ -481,7 +495,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p)
     if (p.lse && lane == 0) p.lse[row] = lse;
 }
 
-template <int D>
+template <int D, bool PAGED>
 hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
 {
     SplitParams p;
@@ -497,12 +511,16 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     p.N_max = a.N_max;
     p.S = a.num_splits;
     p.window = a.window;
+    p.block_table = a.block_table;
+    p.max_blocks = a.max_blocks;
+    p.page_size = a.page_size;
+    p.num_pages = a.num_pages;
     p.rep = a.H / a.H_kv;
     p.ngrp = (p.rep + 15) / 16;               // groups of up to 16 query heads per KV head
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
     const long long gy = (long long)a.H_kv * p.ngrp;
     if (gy > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_split_kernel<D>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     CombineParams cp{a.part_o, a.part_lse, static_cast<uint16_t*>(a.o), a.lse, a.B * a.H, a.num_splits};
@@ -514,8 +532,9 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream)
 {
-    if (a.d == 128) return launch_all<128>(a, stream);
-    if (a.d == 64) return launch_all<64>(a, stream);
+    const bool paged = a.block_table != nullptr;
+    if (a.d == 128) return paged ? launch_all<128, true>(a, stream) : launch_all<128, false>(a, stream);
+    if (a.d == 64) return paged ? launch_all<64, true>(a, stream) : launch_all<64, false>(a, stream);
     return hipErrorInvalidValue;
 }
 

@@ -76,7 +76,9 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
                           const int* seq_lens, void* o, float* lse,
                           int B, int H, int H_kv, int N_max, int d, float scale,
                           int num_splits, void* workspace, size_t workspace_bytes, int window,
-                          hipStream_t stream, const char* name)
+                          hipStream_t stream, const char* name,
+                          const int* block_table = nullptr, int max_blocks = 0, int page_size = 0,
+                          int num_pages = 0)
 {
     fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
     if (s != FA_OK) return s;
@@ -97,7 +99,8 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
     fa::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse,
                      static_cast<float*>(workspace),
                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes),
-                     B, H, H_kv, N_max, d, num_splits, scale, window};
+                     B, H, H_kv, N_max, d, num_splits, scale, window,
+                     block_table, max_blocks, page_size, num_pages};
     char what[64];
     snprintf(what, sizeof what, "%s launch", name);
     return from_hip(fa::launch_decode(a, stream), what);
@@ -177,6 +180,30 @@ fa_status_t fa_decode_window(const void* q, const void* k_cache, const void* v_c
         return fail(FA_ERR_INVALID_ARGUMENT, "window=%d must be at least 1", window);
     return decode_common(q, k_cache, v_cache, seq_lens, o, lse, B, H, H_kv, N_max, d, scale, num_splits,
                          workspace, workspace_bytes, window, stream, "fa_decode_window");
+}
+
+fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int* block_table, int max_blocks, const int* seq_lens,
+                            void* o, float* lse, int B, int H, int H_kv, int num_pages, int page_size,
+                            int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream)
+{
+    if (!block_table)
+        return fail(FA_ERR_INVALID_ARGUMENT, "null block_table");
+    if (!aligned(block_table, 4))
+        return fail(FA_ERR_INVALID_ARGUMENT, "block_table must be 4-byte aligned");
+    if (max_blocks < 1 || num_pages < 1)
+        return fail(FA_ERR_INVALID_ARGUMENT, "max_blocks=%d and num_pages=%d must be at least 1",
+                    max_blocks, num_pages);
+    if (page_size < 1)
+        return fail(FA_ERR_INVALID_ARGUMENT, "page_size=%d must be at least 1", page_size);
+    if (page_size % 16 != 0)
+        return fail(FA_ERR_UNSUPPORTED, "page_size=%d: pages must hold a multiple of 16 rows", page_size);
+    if ((long long)max_blocks * page_size > 0x7fffffffLL || too_large(num_pages, H_kv, page_size, d))
+        return fail(FA_ERR_UNSUPPORTED, "page pool or block table too large");
+    return decode_common(q, k_pages, v_pages, seq_lens, o, lse, B, H, H_kv, max_blocks * page_size, d, scale,
+                         num_splits, workspace, workspace_bytes, 0, stream, "fa_decode_paged", block_table,
+                         max_blocks, page_size, num_pages);
 }
 
 }  // extern "C"

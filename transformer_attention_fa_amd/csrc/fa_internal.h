@@ -34,6 +34,10 @@ struct DecodeArgs {
     int B, H, H_kv, N_max, d, num_splits;
     float scale;
     int window;          // the query sees the last `window` rows, 0 = all
+    // paged cache (block_table != nullptr): k and v are page pools
+    // [num_pages, H_kv, page_size, d]; N_max = max_blocks * page_size
+    const int* block_table = nullptr;   // [B, max_blocks], device
+    int max_blocks = 0, page_size = 0, num_pages = 0;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

@@ -138,6 +138,7 @@ class Decode:
     seed: int
     dtype: str = "bf16"
     window: int = 0       # the query sees the last `window` cached rows; 0 = all
+    page_size: int = 0    # paged cache: rows per page; 0 = contiguous cache
 
     @property
     def scale(self) -> float:
@@ -161,6 +162,8 @@ SWA_PREFILL = Prefill("swa_prefill_b1_h32_hkv8_n16384_w4096_d128", 1, 32, 8, 163
                       window=4096)
 SWA_DECODE = Decode("swa_decode_b32_h32_hkv8_d128_len8k_32k_w4096_s8", 32, 32, 8, 128, 8192, 32768, 32768, 8, 5,
                     window=4096)
+PAGED_DECODE = Decode("paged_decode_b32_h32_hkv8_d128_len8k_32k_p16_s16", 32, 32, 8, 128, 8192, 32768, 32768, 16, 5,
+                      page_size=16)
 CHUNKED_PREFILL = Prefill("chunked_prefill_b4_h32_hkv8_q512_k8192_d128", 4, 32, 8, 512, 8192, 128, True, "bf16", 7)
 
 PREFILL_WORKLOADS = (SINGLE_HEAD_F32, SINGLE_HEAD_F32_CAUSAL, MHA_PREFILL, GQA_PREFILL, MQA_PREFILL)
@@ -235,3 +238,36 @@ def decode_kv_bytes(spec: Decode, seq_lens=None) -> int:
     """Algorithmic KV bytes one decode step reads: sum_b 2*H_kv*len_b*d*2."""
     lens = decode_seq_lens(spec) if seq_lens is None else np.asarray(seq_lens)
     return int(2 * spec.H_kv * spec.d * 2 * int(np.sum(lens.astype(np.int64))))
+
+
+# ---------------------------------------------------------------- paged caches
+def page_table(seq_lens, page_size: int, seed: int, spare: int = 3):
+    """A shuffled page assignment: (block_table [B, max_blocks] int32, num_pages).
+
+    Sequence b needs ceil(len_b / page_size) pages; they are dealt from a seeded
+    permutation of a pool with `spare` extra pages, so neighbouring logical
+    blocks land on unrelated physical pages.  Unused table entries are -1.
+    """
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    need = [int((n + page_size - 1) // page_size) for n in lens]
+    num_pages = sum(need) + spare
+    order = np.random.default_rng([seed, 200]).permutation(num_pages)
+    max_blocks = max(1, max(need))
+    table = np.full((len(lens), max_blocks), -1, np.int32)
+    pos = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = order[pos:pos + nb]
+        pos += nb
+    return table, num_pages
+
+
+def to_pages(cache: np.ndarray, seq_lens, table: np.ndarray, num_pages: int, page_size: int, pad):
+    """Copy rows [0, len_b) of a contiguous cache [B,H_kv,N,d] into a pool
+    [num_pages,H_kv,page_size,d] following `table`; everything else is `pad`."""
+    B, H_kv, N, d = cache.shape
+    pool = np.full((num_pages, H_kv, page_size, d), pad, dtype=cache.dtype)
+    for b, n in enumerate(np.asarray(seq_lens)):
+        for blk in range((int(n) + page_size - 1) // page_size):
+            r0, r1 = blk * page_size, min((blk + 1) * page_size, int(n))
+            pool[table[b, blk], :, :r1 - r0] = cache[b, :, r0:r1]
+    return pool
