@@ -181,3 +181,35 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, scale: float):
     k = gather_pages(k_pages, block_table, seq_lens)
     v = gather_pages(v_pages, block_table, seq_lens)
     return decode(q, k, v, seq_lens, scale)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Decode FP8 E4M3 bytes (the OCP 8-bit format with 4 exponent bits, bias 7,
+    3 mantissa bits, no infinities, NaN = S.1111.111) to float64.
+
+    exponent field 0:     (-1)^s * 2^-6 * m/8        (subnormals and zeros)
+    exponent field 1..15: (-1)^s * 2^(e-7) * (1 + m/8), except e = 15, m = 7: NaN
+    The pages store the KV cache in FP8 without naming the variant; this is the
+    variant MI355X (gfx950) converts in hardware.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+    out = sign * mag
+    out[(e == 15) & ((c & 0x7) == 7)] = np.nan
+    return out
+
+
+def decode_fp8(q, k_codes, v_codes, k_scale: float, v_scale: float, seq_lens, scale: float, window=None):
+    """decode() on an FP8 E4M3 cache with one scale per tensor: the cache holds
+    K / k_scale and V / v_scale, so the attended keys are k_scale * e4m3(K) and
+    the values v_scale * e4m3(V) ("Attention variants" §5: KV cache stored in
+    FP8 to halve the bytes a memory-bound decode step reads)."""
+    k = e4m3_to_f64(k_codes) * float(k_scale)
+    v = e4m3_to_f64(v_codes) * float(v_scale)
+    qd = np.asarray(q)
+    if qd.dtype == np.uint16:
+        qd = (qd.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return decode(np.ascontiguousarray(qd, dtype=np.float64), k, v, seq_lens, scale, window)

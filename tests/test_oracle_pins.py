@@ -576,3 +576,54 @@ def test_paged_decode_equals_contiguous(ps):
         o, l = oracle.decode_paged(q, pool, vpool, table, lens, 0.4)
         np.testing.assert_array_equal(o, o_ref)
         np.testing.assert_array_equal(l, l_ref)
+
+
+# --------------------------------------------------------------------------
+# P-l: FP8 E4M3 KV cache ("Attention variants" §5 KV quantisation).  The
+# decoder is pinned to hand-computed codes, to torch's float8_e4m3fn and to
+# the format's structure; decode_fp8 to decode() on the dequantised cache.
+# --------------------------------------------------------------------------
+def test_e4m3_hand_values():
+    d = oracle.e4m3_to_f64
+    assert d([0x00])[0] == 0.0 and math.copysign(1.0, d([0x80])[0]) == -1.0
+    assert d([0x38])[0] == 1.0                 # e = 7, m = 0
+    assert d([0x40])[0] == 2.0
+    assert d([0x3C])[0] == 1.5                 # m = 4: 1 + 4/8
+    assert d([0x7E])[0] == 448.0               # the largest finite value
+    assert d([0xFE])[0] == -448.0
+    assert d([0x01])[0] == 2.0 ** -9           # the smallest subnormal
+    assert d([0x08])[0] == 2.0 ** -6           # the smallest normal
+    assert np.isnan(d([0x7F])[0]) and np.isnan(d([0xFF])[0])
+
+
+def test_e4m3_matches_torch_and_structure():
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_to_f64(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref)) and int(np.isnan(ours).sum()) == 2
+    fin = ~np.isnan(ours)
+    np.testing.assert_array_equal(ours[fin], ref[fin])
+    pos = ours[:127]                            # codes 0x00..0x7E: increasing
+    assert np.all(np.diff(pos) > 0)
+    np.testing.assert_array_equal(ours[128:255], -ours[:127])
+
+
+def test_decode_fp8_is_decode_on_dequantised_cache():
+    B, H, H_kv, N_max, d = 2, 4, 2, 30, 8
+    rng = np.random.default_rng(151)
+    kc = rng.integers(0, 256, (B, H_kv, N_max, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (B, H_kv, N_max, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x38              # no NaN codes in the attended rows
+    vc[(vc & 0x7F) == 0x7F] = 0x38
+    lens = np.array([7, 30], np.int32)
+    kc[0, :, 7:] = 0x7F                         # rows past a length: NaN codes, never read
+    vc[0, :, 7:] = 0x7F
+    q = rng.standard_normal((B, H, d))
+    o, l = oracle.decode_fp8(q, kc, vc, 0.25, 2.0, lens, 0.3)
+    k = oracle.e4m3_to_f64(kc) * 0.25
+    v = oracle.e4m3_to_f64(vc) * 2.0
+    o2, l2 = oracle.decode(q, k, v, lens, 0.3)
+    np.testing.assert_array_equal(o, o2)
+    np.testing.assert_array_equal(l, l2)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
