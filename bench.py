@@ -168,6 +168,26 @@ def measure_next(dev_bf16, steps, warmup, decode_state=None):
                           "ms_min": mn, "kv_bytes": kv, "page_size": ps, "num_pages": num_pages,
                           "num_splits": spec.num_splits}
         del pools
+        # FP8 E4M3 cache: the same rows quantised per tensor on the device
+        spec = inputs.FP8_DECODE
+        assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
+        codes = []
+        for cache, sc in ((kc, spec.k_scale), (vc, spec.v_scale)):
+            x = (cache.float() * (1.0 / sc)).clamp_(-448.0, 448.0)
+            codes.append(x.to(torch.float8_e4m3fn).view(torch.uint8))
+            del x
+        ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
+                         device=dq.device)
+        avg, med, mn = time_launches(lambda: api.decode_fp8(dq, codes[0], codes[1], spec.k_scale, spec.v_scale, lens,
+                                                            num_splits=spec.num_splits, scale=spec.scale, out=d_o,
+                                                            lse=d_lse, workspace=ws), steps, warmup)
+        kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, seq_lens, elem=1)
+        gbps = kv / (avg * 1e-3) / 1e9
+        out[spec.name] = {"entry": "fa_decode_fp8", "value": gbps, "unit": "GB/s",
+                          "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS, "ms_avg": avg, "ms_median": med,
+                          "ms_min": mn, "kv_bytes": kv, "kv_format": "e4m3, per-tensor scales",
+                          "bf16_equivalent_GBps": 2 * gbps, "num_splits": spec.num_splits}
+        del codes
     return out
 
 

@@ -193,6 +193,25 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
                             int d, float scale, int num_splits, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/*
+ * fa_decode_fp8 -- fa_decode on a KV cache stored in FP8 [AV §5 KV
+ * quantisation: the cache held in FP8 halves the bytes a memory-bound decode
+ * step reads].  The pages name no FP8 variant or scaling; this library takes
+ * OCP FP8 E4M3 (4 exponent bits, bias 7, 3 mantissa bits, no infinities, NaN
+ * = S.1111.111) -- the variant gfx950 converts in hardware -- with one scale per
+ * tensor: key row j is k_scale * e4m3(k_cache[..., j, :]) and value row j is
+ * v_scale * e4m3(v_cache[..., j, :]).  Scores and outputs are computed as in
+ * fa_decode on those dequantised values (the FP8 values convert to bf16
+ * exactly; k_scale folds into the softmax scale and v_scale into the output).
+ *   k_cache, v_cache [B,H_kv,N_max,d] uint8 (E4M3 codes), device, 16-byte aligned
+ *   k_scale, v_scale finite, > 0 (else FA_ERR_INVALID_ARGUMENT)
+ *   q bf16, o bf16, lse fp32, seq_lens, num_splits, workspace: as fa_decode.
+ */
+fa_status_t fa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                          const int* seq_lens, void* o, float* lse, int B, int H, int H_kv, int N_max, int d,
+                          float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(fa_status_t s);
 

@@ -170,3 +170,20 @@ def test_decode_paged_rejects_before_launch(lib, name, change, expect):
                              a["ws"], a["ws_bytes"], None)
     assert st == expect, (name, st, lib.fa_last_error())
     assert lib.fa_last_error()
+
+
+
+@pytest.mark.parametrize("k_scale,v_scale", [(0.0, 1.0), (1.0, -1.0), (float("nan"), 1.0), (1.0, float("inf"))])
+def test_decode_fp8_rejects_bad_scales(lib, k_scale, v_scale):
+    a = GOOD_DEC
+    st = lib.fa_decode_fp8(a["q"], a["k"], a["v"], k_scale, v_scale, a["lens"], a["o"], a["lse"], a["B"], a["H"],
+                           a["H_kv"], a["N_max"], a["d"], a["scale"], a["S"], a["ws"], a["ws_bytes"], None)
+    assert st == INVALID and b"scale" in lib.fa_last_error()
+
+
+@pytest.mark.parametrize("name,change,expect", DEC_CASES, ids=[c[0] for c in DEC_CASES])
+def test_decode_fp8_rejects_before_launch(lib, name, change, expect):
+    a = dict(GOOD_DEC, **change)
+    st = lib.fa_decode_fp8(a["q"], a["k"], a["v"], 0.5, 0.5, a["lens"], a["o"], a["lse"], a["B"], a["H"],
+                           a["H_kv"], a["N_max"], a["d"], a["scale"], a["S"], a["ws"], a["ws_bytes"], None)
+    assert st == expect, (name, st, lib.fa_last_error())

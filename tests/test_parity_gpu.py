@@ -420,3 +420,61 @@ def test_decode_paged_workload_full_compare():
     torch.cuda.synchronize()
     o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale)
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+# ------------------------------------------------------------------ FP8 KV cache
+def _fp8_run(data, num_splits, k_scale, v_scale):
+    import torch
+    s = data.spec
+    q = bf16_to_device(data.q)
+    kc = torch.from_numpy(data.k_cache).cuda()
+    vc = torch.from_numpy(data.v_cache).cuda()
+    o, lse = api.decode_fp8(q, kc, vc, k_scale, v_scale, torch.from_numpy(data.seq_lens).cuda(),
+                            num_splits=num_splits, scale=s.scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+@pytest.mark.parametrize("H,H_kv,d", [(8, 2, 128), (16, 1, 64), (12, 4, 128), (40, 2, 128)])
+@pytest.mark.parametrize("num_splits", [1, 7, 16])
+def test_decode_fp8(H, H_kv, d, num_splits):
+    spec = inputs.Decode(f"fp8_B6_H{H}_Hkv{H_kv}_d{d}", 6, H, H_kv, d, 1, 3000, 3000, num_splits, 61,
+                         dtype="e4m3", k_scale=2.0 ** -6, v_scale=2.0 ** -5)
+    lens = np.array([1, 2, 15, 16, 17, 3000], np.int32)
+    data = inputs.decode_inputs_fp8(spec, seq_lens=lens)
+    o, lse = _fp8_run(data, num_splits, spec.k_scale, spec.v_scale)
+    o_ref, lse_ref = oracle.decode_fp8(data.q, data.k_cache, data.v_cache, spec.k_scale, spec.v_scale, lens,
+                                       spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+def test_decode_fp8_every_code():
+    """Random codes over the whole finite range (subnormals, zeros of both signs,
+    +-448) with scales that are not powers of two."""
+    import torch
+    B, H, H_kv, N, d = 2, 8, 2, 700, 128
+    rng = np.random.default_rng(67)
+    kc = rng.integers(0, 256, (B, H_kv, N, d)).astype(np.uint8)
+    vc = rng.integers(0, 256, (B, H_kv, N, d)).astype(np.uint8)
+    kc[(kc & 0x7F) == 0x7F] = 0x00       # the NaN codes become zeros
+    vc[(vc & 0x7F) == 0x7F] = 0x80
+    q = inputs.f32_to_bf16_bits(rng.standard_normal((B, H, d), dtype=np.float32) * np.float32(0.05))
+    lens = np.array([333, 700], np.int32)
+    k_scale, v_scale = 0.0123, 0.37
+    spec = inputs.Decode("fp8_codes", B, H, H_kv, d, 1, N, N, 8, 0, dtype="e4m3")
+    data = inputs.DecodeData(spec, q, kc, vc, lens)
+    o, lse = _fp8_run(data, 8, k_scale, v_scale)
+    o_ref, lse_ref = oracle.decode_fp8(q, kc, vc, k_scale, v_scale, lens, spec.scale)
+    # values up to 448 * 0.37: the O tolerance scales with the value range (bf16 output rounding)
+    tol = BF16_O_TOL * float(np.max(np.abs(o_ref)))
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, max(tol, BF16_O_TOL), BF16_LSE_REL_TOL, label="every code")
+
+
+def test_decode_fp8_workload_full_compare():
+    spec = inputs.FP8_DECODE
+    say(f"fa_decode_fp8 full-size workload {spec.name}")
+    data = inputs.decode_inputs_fp8(spec)
+    o, lse = _fp8_run(data, spec.num_splits, spec.k_scale, spec.v_scale)
+    o_ref, lse_ref = oracle.decode_fp8(data.q, data.k_cache, data.v_cache, spec.k_scale, spec.v_scale,
+                                       data.seq_lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)

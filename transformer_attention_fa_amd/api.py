@@ -8,7 +8,7 @@ or a call fails, an exception is raised.
 Entry points mirror the C names: ``fwd`` (fa_fwd, bf16; with ``window=W``
 fa_fwd_window), ``fwd_f32`` (fa_fwd_f32), ``decode`` (fa_decode; with
 ``window=W`` fa_decode_window), ``decode_paged`` (fa_decode_paged),
-``decode_workspace_bytes``.
+``decode_fp8`` (fa_decode_fp8), ``decode_workspace_bytes``.
 ``scale=None`` means 1/sqrt(d), like the ``softmax_scale=None`` default of the
 flash_attn_func usage shown in "Attention mechanism evolution: MHA -> MLA,
 Flash Attention" (toolsku.com), Flash Attention section.
@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
 EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode", "fa_decode_window", "fa_decode_paged",
-            "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error")
+            "fa_decode_fp8", "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error")
 
 _lib = None
 
@@ -60,6 +60,8 @@ def load():
     lib.fa_decode_window.restype = i
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode_paged.restype = i
+    lib.fa_decode_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
+    lib.fa_decode_fp8.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -241,4 +243,41 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits: int = 1
                                      block_table.shape[1], seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t),
                                      B, H, H_kv, num_pages, page_size, d, float(scale), int(num_splits),
                                      workspace.data_ptr(), workspace.numel(), _stream(q.device)))
+    return out, lse_t
+
+
+def decode_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, seq_lens, num_splits: int = 16,
+               scale: float | None = None, out=None, lse=None, workspace=None):
+    """fa_decode_fp8: q [B,H,d] bf16; caches [B,H_kv,N_max,d] uint8 E4M3 codes with
+    per-tensor scales (keys k_scale * code, values v_scale * code)."""
+    torch = _torch()
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_cache, "k_cache", torch.uint8, 4, q.device)
+    _require(v_cache, "v_cache", torch.uint8, 4, q.device)
+    _require(seq_lens, "seq_lens", torch.int32, 1, q.device)
+    B, H, d = q.shape
+    Bk, H_kv, N_max, dk = k_cache.shape
+    if Bk != B or dk != d or tuple(v_cache.shape) != tuple(k_cache.shape) or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, 3, q.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    elif lse is not False:
+        _require(lse, "lse", torch.float32, 2, q.device)
+    lse_t = None if lse is False else lse
+    with torch.cuda.device(q.device):
+        check(load().fa_decode_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), float(k_scale),
+                                   float(v_scale), seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t), B, H, H_kv,
+                                   N_max, d, float(scale), int(num_splits), workspace.data_ptr(), workspace.numel(),
+                                   _stream(q.device)))
     return out, lse_t

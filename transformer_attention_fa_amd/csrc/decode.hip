@@ -70,8 +70,8 @@ constexpr int kStreamPolicy = 2;
 
 struct SplitParams {
     const uint16_t* q;
-    const uint16_t* k;
-    const uint16_t* v;
+    const char* k;          // cache (or page pool) bytes: bf16, or FP8 E4M3 codes
+    const char* v;
     const int* seq_lens;
     float* part_o;
     float* part_lse;
@@ -81,7 +81,8 @@ struct SplitParams {
     // row r of sequence b is row r % page_size of page block_table[b, r / page_size]
     const int* block_table;
     int max_blocks, page_size, num_pages;
-    float c;      // scale * log2(e), > 0
+    float c;      // scale * log2(e) (times k_scale for an FP8 cache), > 0
+    float v_scale;          // FP8 cache: values are v_scale * e4m3 code; 1 otherwise
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -105,6 +106,16 @@ __device__ __forceinline__ int dswz(int r, int c)
 {
     if constexpr (D == 128) return c ^ (2 * (r & 7) + ((r >> 3) & 1));
     else return c ^ (2 * ((r >> 1) & 3) + ((r >> 3) & 1));
+}
+
+// Position of 16-byte chunk c of row r (0..15) of a 16-key FP8 tile (rows of D
+// bytes).  Conflict free for the 8-byte K fragment reads (16 rows, the two
+// halves of one chunk per row pair of lanes) on the 64-bank LDS.
+template <int D>
+__device__ __forceinline__ int fswz(int r, int c)
+{
+    if constexpr (D == 128) return c ^ ((r >> 1) & 7);
+    else return c ^ ((r >> 2) & 3);
 }
 
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
@@ -213,18 +224,76 @@ __device__ __forceinline__ int sequence_for(const SplitParams& p, int z)
     return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
 }
 
-template <int D, bool PAGED>
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// KS 8-byte LDS reads (FP8 K fragments), waiting for their own results
+template <int N>
+__device__ __forceinline__ void lds_read_b64n(u32x2 (&a)[N], const unsigned (&p)[N])
+{
+    if constexpr (N == 4)
+        asm volatile("ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\tds_read_b64 %3, %7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+                     : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+                     : "memory");
+    else
+        asm volatile("ds_read_b64 %0, %2\n\tds_read_b64 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(a[0]), "=&v"(a[1])
+                     : "v"(p[0]), "v"(p[1])
+                     : "memory");
+}
+// N 16-byte LDS reads, waiting for their own results
+template <int N>
+__device__ __forceinline__ void lds_read_b128n(u32x4 (&a)[N], const unsigned (&p)[N])
+{
+    if constexpr (N == 2)
+        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     : "=&v"(a[0]), "=&v"(a[1])
+                     : "v"(p[0]), "v"(p[1])
+                     : "memory");
+    else
+        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(a[0]) : "v"(p[0]) : "memory");
+}
+// N 16-byte LDS writes, complete before the block ends
+template <int N>
+__device__ __forceinline__ void lds_write_b128n(const unsigned (&p)[N], const u32x4 (&a)[N])
+{
+    if constexpr (N == 4)
+        asm volatile("ds_write_b128 %0, %4\n\tds_write_b128 %1, %5\n\tds_write_b128 %2, %6\n\tds_write_b128 %3, %7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     :
+                     : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(a[0]), "v"(a[1]), "v"(a[2]), "v"(a[3])
+                     : "memory");
+    else
+        asm volatile("ds_write_b128 %0, %2\n\tds_write_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                     :
+                     : "v"(p[0]), "v"(p[1]), "v"(a[0]), "v"(a[1])
+                     : "memory");
+}
+
+// four FP8 E4M3 codes -> four bf16 (exact: every E4M3 value is a bf16 value)
+__device__ __forceinline__ unsigned long long e4m3x4_to_bf16x4(unsigned w)
+{
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+    const bf16x4 r = __builtin_convertvector((f32x4{lo[0], lo[1], hi[0], hi[1]}), bf16x4);
+    return __builtin_bit_cast(unsigned long long, r);
+}
+
+template <int D, bool PAGED, bool KV8>
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
 {
     constexpr int NW = 4;
     constexpr int TK = 16;                   // keys per tile
-    constexpr int ROWB = D * 2;
-    constexpr int CPR = D / 8;               // 16-byte chunks per row
+    constexpr int ROWB = KV8 ? D : D * 2;    // bytes per cache row
+    constexpr int QROWB = D * 2;             // bytes per query row (bf16)
+    constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
     constexpr int TILEB = TK * ROWB;         // bytes per K (or V) tile
     constexpr int LOADS = TILEB / (64 * 16); // wave load instructions per tensor per tile
     constexpr int KS = D / 32;               // 16x16x32 k-steps over d
     constexpr int DB = D / 16;               // 16-row blocks of d for O^T
-    constexpr int WAVE_LDS = 2 * 2 * TILEB;  // two stages of (K, V) per wave
+    constexpr int VSTAGE = 2 * 2 * TILEB;    // FP8: bf16 copy of the V tile, after the two stages
+    constexpr int WAVE_LDS = 2 * 2 * TILEB + (KV8 ? TK * D * 2 : 0);
     static_assert(TILEB % (64 * 16) == 0, "tile shape");
 
     constexpr int QB = 16 * 256;             // Q rows of the head group (16 x 256 B at most)
@@ -250,8 +319,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     const int nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles w, w+4, ...
 
     const size_t kv_row0 = PAGED ? 0 : ((size_t)b * p.H_kv + g) * (size_t)p.N_max + (size_t)j0;
-    const char* kbase = reinterpret_cast<const char*>(p.k + kv_row0 * D);
-    const char* vbase = reinterpret_cast<const char*>(p.v + kv_row0 * D);
+    const char* kbase = p.k + kv_row0 * ROWB;
+    const char* vbase = p.v + kv_row0 * ROWB;
     char* wl = lds + w * WAVE_LDS;
 
     int ld_off[LOADS];
@@ -259,7 +328,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     for (int i = 0; i < LOADS; ++i) {
         const int pos = i * 64 + lane;
         const int r = pos / CPR, cp = pos % CPR;
-        ld_off[i] = r * ROWB + dswz<D>(r, cp) * 16;
+        ld_off[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : dswz<D>(r, cp)) * 16;
     }
     // tile t of the chunk into stage s: rows past the chunk read as 0
     auto issue = [&](int t, int s) __attribute__((always_inline)) {
@@ -287,13 +356,31 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     // per-lane LDS read offsets inside a stage
     int k_off[KS];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) k_off[ks] = l16 * ROWB + dswz<D>(l16, 4 * ks + g4) * 16;
+    for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (KV8)     // 8 bytes: d = 32*ks + 8*g4 .. +8 = half (g4 & 1) of chunk 2*ks + g4/2
+            k_off[ks] = l16 * ROWB + fswz<D>(l16, 2 * ks + (g4 >> 1)) * 16 + (g4 & 1) * 8;
+        else
+            k_off[ks] = l16 * ROWB + dswz<D>(l16, 4 * ks + g4) * 16;
+    }
+    // V^T fragments through transposing reads of a bf16 tile: the V tile of the
+    // stage, or (FP8) the wave's bf16 copy of it
     int v_off[DB];
     {
         const int r = 4 * g4 + (l16 >> 2);
 #pragma unroll
         for (int dm = 0; dm < DB; ++dm)
-            v_off[dm] = TILEB + r * ROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 + (l16 & 1) * 8;
+            v_off[dm] = (KV8 ? VSTAGE : TILEB) + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 +
+                        (l16 & 1) * 8;
+    }
+    // FP8: lane l converts row l/4 of the V tile, d = (l%4)*D/4 .. +D/4
+    constexpr int CV = D / 64;               // 16-byte FP8 chunks per lane
+    unsigned cv_src[CV], cv_dst[2 * CV];
+    if constexpr (KV8) {
+        const int r = lane >> 2, part = lane & 3;
+#pragma unroll
+        for (int i = 0; i < CV; ++i) cv_src[i] = TILEB + r * ROWB + fswz<D>(r, part * CV + i) * 16;
+#pragma unroll
+        for (int i = 0; i < 2 * CV; ++i) cv_dst[i] = VSTAGE + r * QROWB + dswz<D>(r, part * 2 * CV + i) * 16;
     }
 
     f32x4 oacc[DB];
@@ -305,7 +392,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     // group read as 0), then the first two tiles of this wave
     char* qs = lds + NW * WAVE_LDS;
     {
-        const i32x4 rq = make_rsrc(p.q + ((size_t)b * p.H + h0) * D, (unsigned)nh * ROWB);
+        const i32x4 rq = make_rsrc(p.q + ((size_t)b * p.H + h0) * D, (unsigned)nh * QROWB);
         fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, w * 1024 + lane * 16, 0, 0, 0);
     }
     if (nt_w > 0) issue(w, 0);
@@ -317,7 +404,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     // Q^T fragments (B of S^T): head l16, d = 32*ks + 8*g4 .. +8
     bf16x8 qf[KS];
     {
-        const unsigned qa = (unsigned)(uintptr_t)(LDS_AS char*)qs + l16 * ROWB + g4 * 16;
+        const unsigned qa = (unsigned)(uintptr_t)(LDS_AS char*)qs + l16 * QROWB + g4 * 16;
         if constexpr (KS == 4) lds_read_k4(qf, qa, qa + 64, qa + 128, qa + 192);
         else lds_read_k2(qf, qa, qa + 64);
     }
@@ -326,14 +413,44 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     auto compute = [&](int t, int s) __attribute__((always_inline)) {
         const unsigned st = wl_addr + s * 2 * TILEB;
         bf16x8 kf[KS];
-        if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
-        else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
+        if constexpr (KV8) {
+            unsigned ka[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) ka[ks] = st + k_off[ks];
+            u32x2 k8[KS];
+            lds_read_b64n<KS>(k8, ka);
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const unsigned long long lo = e4m3x4_to_bf16x4(k8[ks][0]), hi = e4m3x4_to_bf16x4(k8[ks][1]);
+                kf[ks] = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
+                                                           (unsigned)(hi >> 32)}));
+            }
+            // V tile: FP8 codes -> the wave's bf16 copy, laid out like a bf16 tile
+            unsigned va[CV], wa[2 * CV];
+#pragma unroll
+            for (int i = 0; i < CV; ++i) va[i] = st + cv_src[i];
+#pragma unroll
+            for (int i = 0; i < 2 * CV; ++i) wa[i] = wl_addr + cv_dst[i];
+            u32x4 v8[CV], vb[2 * CV];
+            lds_read_b128n<CV>(v8, va);
+#pragma unroll
+            for (int i = 0; i < CV; ++i)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const unsigned long long a = e4m3x4_to_bf16x4(v8[i][2 * h]), c2 = e4m3x4_to_bf16x4(v8[i][2 * h + 1]);
+                    vb[2 * i + h] = u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)c2, (unsigned)(c2 >> 32)};
+                }
+            lds_write_b128n<2 * CV>(wa, vb);
+        } else {
+            if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
+            else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
+        }
         f32x4 sc = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
         unsigned vaddr[DB];
 #pragma unroll
-        for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
+        for (int dm = 0; dm < DB; ++dm) vaddr[dm] = (KV8 ? wl_addr : st) + v_off[dm];
         i16x4 vf[DB];
         if constexpr (DB == 8) lds_read_vt8(vf, vaddr);
         else lds_read_vt4(vf, vaddr);
@@ -401,7 +518,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
             oo += a * sh_o[(ww * 16 + hh) * D + d];
         }
         const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
-        p.part_o[row * D + d] = ll > 0.f ? oo / ll : 0.f;
+        p.part_o[row * D + d] = ll > 0.f ? oo / ll * p.v_scale : 0.f;
         if (d == 0) p.part_lse[row] = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
     }
 }
@@ -495,13 +612,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p)
     if (p.lse && lane == 0) p.lse[row] = lse;
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool KV8>
 hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
 {
     SplitParams p;
     p.q = static_cast<const uint16_t*>(a.q);
-    p.k = static_cast<const uint16_t*>(a.k);
-    p.v = static_cast<const uint16_t*>(a.v);
+    p.k = static_cast<const char*>(a.k);
+    p.v = static_cast<const char*>(a.v);
     p.seq_lens = a.seq_lens;
     p.part_o = a.part_o;
     p.part_lse = a.part_lse;
@@ -517,10 +634,12 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     p.num_pages = a.num_pages;
     p.rep = a.H / a.H_kv;
     p.ngrp = (p.rep + 15) / 16;               // groups of up to 16 query heads per KV head
-    p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
+    const float sc = KV8 ? a.scale * a.k_scale : a.scale;   // FP8: keys are k_scale * code
+    p.c = sc > 0.f ? sc * kLog2e : 1e-30f;
+    p.v_scale = KV8 ? a.v_scale : 1.f;
     const long long gy = (long long)a.H_kv * p.ngrp;
     if (gy > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((decode_split_kernel<D, PAGED>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<D, PAGED, KV8>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     CombineParams cp{a.part_o, a.part_lse, static_cast<uint16_t*>(a.o), a.lse, a.B * a.H, a.num_splits};
@@ -533,8 +652,14 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream)
 {
     const bool paged = a.block_table != nullptr;
-    if (a.d == 128) return paged ? launch_all<128, true>(a, stream) : launch_all<128, false>(a, stream);
-    if (a.d == 64) return paged ? launch_all<64, true>(a, stream) : launch_all<64, false>(a, stream);
+    if (a.kv_fp8) {
+        if (paged) return hipErrorInvalidValue;        // not offered
+        if (a.d == 128) return launch_all<128, false, true>(a, stream);
+        if (a.d == 64) return launch_all<64, false, true>(a, stream);
+        return hipErrorInvalidValue;
+    }
+    if (a.d == 128) return paged ? launch_all<128, true, false>(a, stream) : launch_all<128, false, false>(a, stream);
+    if (a.d == 64) return paged ? launch_all<64, true, false>(a, stream) : launch_all<64, false, false>(a, stream);
     return hipErrorInvalidValue;
 }
 

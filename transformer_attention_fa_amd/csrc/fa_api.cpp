@@ -78,7 +78,7 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
                           int num_splits, void* workspace, size_t workspace_bytes, int window,
                           hipStream_t stream, const char* name,
                           const int* block_table = nullptr, int max_blocks = 0, int page_size = 0,
-                          int num_pages = 0)
+                          int num_pages = 0, int kv_fp8 = 0, float k_scale = 1.f, float v_scale = 1.f)
 {
     fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
     if (s != FA_OK) return s;
@@ -100,7 +100,7 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
                      static_cast<float*>(workspace),
                      reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes),
                      B, H, H_kv, N_max, d, num_splits, scale, window,
-                     block_table, max_blocks, page_size, num_pages};
+                     block_table, max_blocks, page_size, num_pages, kv_fp8, k_scale, v_scale};
     char what[64];
     snprintf(what, sizeof what, "%s launch", name);
     return from_hip(fa::launch_decode(a, stream), what);
@@ -204,6 +204,19 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
     return decode_common(q, k_pages, v_pages, seq_lens, o, lse, B, H, H_kv, max_blocks * page_size, d, scale,
                          num_splits, workspace, workspace_bytes, 0, stream, "fa_decode_paged", block_table,
                          max_blocks, page_size, num_pages);
+}
+
+fa_status_t fa_decode_fp8(const void* q, const void* k_cache, const void* v_cache, float k_scale, float v_scale,
+                          const int* seq_lens, void* o, float* lse, int B, int H, int H_kv, int N_max, int d,
+                          float scale, int num_splits, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream)
+{
+    if (!std::isfinite(k_scale) || !std::isfinite(v_scale) || k_scale <= 0.f || v_scale <= 0.f)
+        return fail(FA_ERR_INVALID_ARGUMENT, "k_scale=%g and v_scale=%g must be finite and positive",
+                    (double)k_scale, (double)v_scale);
+    return decode_common(q, k_cache, v_cache, seq_lens, o, lse, B, H, H_kv, N_max, d, scale, num_splits,
+                         workspace, workspace_bytes, 0, stream, "fa_decode_fp8", nullptr, 0, 0, 0, 1, k_scale,
+                         v_scale);
 }
 
 }  // extern "C"

@@ -38,6 +38,10 @@ struct DecodeArgs {
     // [num_pages, H_kv, page_size, d]; N_max = max_blocks * page_size
     const int* block_table = nullptr;   // [B, max_blocks], device
     int max_blocks = 0, page_size = 0, num_pages = 0;
+    // FP8 E4M3 cache (kv_fp8 != 0): k and v hold codes; keys are k_scale * code,
+    // values v_scale * code
+    int kv_fp8 = 0;
+    float k_scale = 1.f, v_scale = 1.f;
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);

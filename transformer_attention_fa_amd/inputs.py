@@ -139,6 +139,8 @@ class Decode:
     dtype: str = "bf16"
     window: int = 0       # the query sees the last `window` cached rows; 0 = all
     page_size: int = 0    # paged cache: rows per page; 0 = contiguous cache
+    k_scale: float = 1.0  # FP8 cache (dtype "e4m3"): keys are k_scale * code
+    v_scale: float = 1.0  # ... and values v_scale * code
 
     @property
     def scale(self) -> float:
@@ -164,6 +166,8 @@ SWA_DECODE = Decode("swa_decode_b32_h32_hkv8_d128_len8k_32k_w4096_s8", 32, 32, 8
                     window=4096)
 PAGED_DECODE = Decode("paged_decode_b32_h32_hkv8_d128_len8k_32k_p16_s16", 32, 32, 8, 128, 8192, 32768, 32768, 16, 5,
                       page_size=16)
+FP8_DECODE = Decode("fp8_decode_b32_h32_hkv8_d128_len8k_32k_s16", 32, 32, 8, 128, 8192, 32768, 32768, 16, 5,
+                    dtype="e4m3", k_scale=2.0 ** -6, v_scale=2.0 ** -6)
 CHUNKED_PREFILL = Prefill("chunked_prefill_b4_h32_hkv8_q512_k8192_d128", 4, 32, 8, 512, 8192, 128, True, "bf16", 7)
 
 PREFILL_WORKLOADS = (SINGLE_HEAD_F32, SINGLE_HEAD_F32_CAUSAL, MHA_PREFILL, GQA_PREFILL, MQA_PREFILL)
@@ -271,3 +275,36 @@ def to_pages(cache: np.ndarray, seq_lens, table: np.ndarray, num_pages: int, pag
             r0, r1 = blk * page_size, min((blk + 1) * page_size, int(n))
             pool[table[b, blk], :, :r1 - r0] = cache[b, :, r0:r1]
     return pool
+
+
+# ---------------------------------------------------------------- FP8 caches
+E4M3_NAN = 0x7F
+
+
+def f32_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """FP8 E4M3 codes of float32 values: round to nearest even, saturated at
+    +-448 (torch's float8_e4m3fn cast does the rounding)."""
+    import torch
+    x = np.clip(np.asarray(x, dtype=np.float32), -448.0, 448.0)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def decode_inputs_fp8(spec: Decode, seq_lens=None) -> DecodeData:
+    """q (bf16 bits) and FP8 E4M3 caches (codes of value / scale) for a decode
+    workload; the same draws as decode_inputs, quantised per tensor.  Rows at or
+    past a length hold the NaN code."""
+    lens = decode_seq_lens(spec) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
+    if lens.shape != (spec.B,) or lens.min() < 1 or lens.max() > spec.N_max:
+        raise ValueError("seq_lens must hold B values in 1..N_max")
+    q = f32_to_bf16_bits(np.random.default_rng([spec.seed, 0]).standard_normal((spec.B, spec.H, spec.d),
+                                                                              dtype=np.float32))
+    caches = []
+    for tag, sc in ((1, spec.k_scale), (2, spec.v_scale)):
+        f = _normal_blocks(spec.seed, tag, spec.B, spec.H_kv, (spec.N_max, spec.d), rows=lens)
+        f *= np.float32(1.0 / sc)
+        c = f32_to_e4m3_codes(f)
+        del f
+        for b in range(spec.B):
+            c[b, :, int(lens[b]):, :] = E4M3_NAN
+        caches.append(c)
+    return DecodeData(spec, q, caches[0], caches[1], lens)
