@@ -37,9 +37,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
                     help="skip the sliding-window and chunked-prefill measurements (the 'next' object)")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
-                    help="time one half of the step only (for profiling runs); 'copy' runs a plain "
-                         "1 GiB device-to-device copy, the reference for scaling HBM byte counters")
+    ap.add_argument("--only", choices=["prefill", "decode", "next", "copy"], default=None,
+                    help="time one part only (for profiling runs): one half of the step, the 'next' "
+                         "workloads, or 'copy', a plain 1 GiB device-to-device copy (the reference for "
+                         "scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -191,6 +192,22 @@ def measure_next(dev_bf16, steps, warmup, decode_state=None):
     return out
 
 
+def add_rooflines(nxt):
+    """Roofline objects for the 'next' entries (traffic from the committed counters when current)."""
+    from transformer_attention_fa_amd import roofline
+    for name, r in nxt.items():
+        if r["unit"] == "TFLOP/s":
+            r["roofline"] = {"bound": "mfma", "achieved": r["value"], "peak": roofline.PEAK_BF16_TFLOPS,
+                             "unit": "TFLOP/s", "frac": r["value"] / roofline.PEAK_BF16_TFLOPS,
+                             "traffic": traffic_for(f"fwd_bf16:{name}", ["fwd_bf16.hip"]), "kernel": "fwd_bf16_kernel"}
+        else:
+            r["roofline"] = {"bound": "hbm", "achieved": r["value"], "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
+                             "frac": r["value"] / roofline.PEAK_HBM_GBPS,
+                             "traffic": traffic_for(f"decode:{name}", ["decode.hip"]),
+                             "kernel": "decode_split_kernel + decode_combine_kernel"}
+    return nxt
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -217,7 +234,7 @@ def main():
     pspec = {"mha": inputs.MHA_PREFILL, "gqa": inputs.GQA_PREFILL, "mqa": inputs.MQA_PREFILL}[args.workload]
     dspec = inputs.GQA_DECODE
     do_prefill = args.only in (None, "prefill")
-    do_decode = args.only in (None, "decode")
+    do_decode = args.only in (None, "decode", "next")     # 'next' reuses the decode caches
 
     def dev_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -255,6 +272,12 @@ def main():
             if ev is not None:
                 ev[3].record()
 
+    if args.only == "next":
+        rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+               "next": add_rooflines(measure_next(dev_bf16, args.steps, args.warmup,
+                                                  (dq, kc, vc, lens, seq_lens, dspec)))}
+        print(json.dumps(rec), flush=True)
+        return
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -304,8 +327,8 @@ def main():
             rec.update({"value": gbps, "unit": "GB/s"})
     rec["config"] = config
     if args.only is None and not args.no_next:
-        rec["next"] = measure_next(dev_bf16, args.steps, args.warmup,
-                                   (dq, kc, vc, lens, seq_lens, dspec) if do_decode else None)
+        rec["next"] = add_rooflines(measure_next(dev_bf16, args.steps, args.warmup,
+                                                 (dq, kc, vc, lens, seq_lens, dspec) if do_decode else None))
     if do_prefill and not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(pspec, n_batches=pspec.B)
     props = torch.cuda.get_device_properties(dev)
