@@ -474,27 +474,42 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     }
     for (; j <= nkb; ++j) run_period(j, C0{}, C0{}, C0{});  // tiles after this wave's rows
 
-    // ---- epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l)
+    // ---- epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l).  A lane
+    //      holds 4-element pieces of one row, so storing straight from the
+    //      accumulators writes 32 rows x 8 bytes per instruction.  Instead each
+    //      wave stages its 32 x D tile in LDS (16-byte chunks XOR-swizzled by
+    //      row) and reads it back row-major: every global store is then 4 (or
+    //      8) whole rows, 1 KB contiguous.
     float l_tot;
     {
         const float l_run = l_a + l_b;
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
         l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    if (qi < p.N_q) {
-        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        uint16_t* dst = p.o + (q_row0 + qi) * D;
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (p.lse && half == 0 && qi < p.N_q)
+        p.lse[q_row0 + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+    static_assert(BM * ROWB <= 4 * TILE, "the output tile is staged in the K/V slots");
+    __syncthreads();                               // every wave is done with the K/V slots
+    char* ow = lds + w * 32 * ROWB;                // this wave's 32 rows
 #pragma unroll
-        for (int dm = 0; dm < DBLK; ++dm)
+    for (int dm = 0; dm < DBLK; ++dm)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                f32x4 t;
+        for (int gq = 0; gq < 4; ++gq) {
+            f32x4 t;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
-                *reinterpret_cast<bf16x4*>(dst + dm * 32 + gq * 8 + half * 4) = __builtin_convertvector(t, bf16x4);
-            }
-        if (p.lse && half == 0)
-            p.lse[q_row0 + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+            for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
+            const int c = 4 * dm + gq;             // 16-byte chunk of the row (elements 8c .. 8c+7)
+            *reinterpret_cast<bf16x4*>(ow + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
+                __builtin_convertvector(t, bf16x4);
+        }
+    constexpr int RPI = 64 / CPR;                  // rows per wave-wide 16-byte read
+#pragma unroll
+    for (int k = 0; k < 32 / RPI; ++k) {
+        const int r = k * RPI + lane / CPR, c = lane % CPR;
+        const u32x4 t = *reinterpret_cast<const u32x4*>(ow + r * ROWB + ((c ^ (r & (CPR - 1))) * 16));
+        if (qw0 + r < p.N_q)
+            *reinterpret_cast<u32x4*>(p.o + (q_row0 + qw0 + r) * D + c * 8) = t;
     }
 }
 
