@@ -11,8 +11,10 @@
 // (toolsku.com) GQA code).
 //
 // gfx950 mapping (not from the pages, whose kernel targets other GPUs):
-//  * workgroup = 8 waves, BM = 256 query rows, each wave owns 32 rows; two
-//    waves share each SIMD;
+//  * persistent grid: one workgroup per resident slot (256 CUs x 1 on
+//    MI355X), each working through a list of items (query block of BM = 256
+//    rows, head, batch); workgroup = 8 waves, each wave owns 32 rows of the
+//    block; two waves share each SIMD;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    (A = K fragment from LDS, B = Q fragment held in VGPRs for the whole
 //    kernel).  In the 32x32 accumulator layout lane l holds column l%32 -- one
@@ -42,10 +44,17 @@
 //    maximum exceeds it by more than 8 (so every exp2 argument stays <= 8 and
 //    p <= 256); the result is the same quantity, O = sum p v / sum p, with the
 //    common factor chosen differently; lse = ln2 * (m + log2 l);
-//  * workgroup order: workgroups go to the 8 XCDs round robin; the index is
-//    remapped so each XCD works through a contiguous range of heads (shared
-//    K/V stays in that XCD's L2), longest causal query blocks first within a
-//    group of `group` heads.
+//  * item order: workgroups sit on the 8 XCDs round robin; each XCD works
+//    through a contiguous range of heads (shared K/V stays in that XCD's L2),
+//    longest causal query blocks first within a group of `group` heads, and
+//    its workgroups take the list in rounds that alternate direction (a long
+//    causal block in one round pairs with a short one in the next);
+//  * item switch without a cold start: while an item runs, the next item's Q
+//    block streams into its own LDS area (one slice per period) and its first
+//    K tile into the K slot the last period leaves free; at the switch each
+//    wave takes its Q fragments from that area, then stages its finished
+//    32 x d output tile in the same rows and stores it as whole rows, and the
+//    next item's first period starts without waiting for those stores.
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -89,7 +98,9 @@ struct Params {
     int rep;      // H / H_kv
     int nqb;      // query blocks per head
     int window;   // sliding window in keys (causal only); 0 = none
-    int group;    // heads per longest-first group of the workgroup order
+    int group;    // heads per longest-first group of the item order
+    int items;    // work items (query blocks x heads x batch)
+    int grid;     // workgroups of the persistent grid
     float c;      // scale * log2(e), > 0
 };
 
@@ -151,11 +162,11 @@ __device__ __forceinline__ void decompose(int id, const Params& p, bool causal, 
     b = bh / p.H;
 }
 
-template <int D, int NW, bool CAUSAL>
+template <int D, int NW, bool CAUSAL, bool PERSIST>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 {
     static_assert(NW == 8, "the two wave groups pair up on the four SIMDs");
-    constexpr int BM = NW * 32;              // query rows per workgroup
+    constexpr int BM = NW * 32;              // query rows per work item
     constexpr int NTHR = NW * 64;
     constexpr int BN = 64;                   // keys per LDS tile
     constexpr int KSTEPS = D / 16;           // MFMA k-steps over d for S^T
@@ -165,11 +176,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     constexpr int CPR = D / 8;               // 16-byte chunks per row
     constexpr int TILE = BN * ROWB;          // bytes per K (or V) tile
     constexpr int LOADS = TILE / (NTHR * 16);
-    static_assert(TILE % (NTHR * 16) == 0, "tile must be a whole number of wave loads");
+    constexpr int QTILE = BM * ROWB;         // bytes of a Q block (the Q area)
+    constexpr int QPARTS = QTILE / (NTHR * 16);
+    static_assert(TILE % (NTHR * 16) == 0 && QTILE % (NTHR * 16) == 0, "tiles must be whole workgroup loads");
     static_assert(D % 32 == 0, "tile shape");
 
-    // [K slot 0, K slot 1, V slot 0, V slot 1]
-    __shared__ __attribute__((aligned(1024))) char lds[4 * TILE];
+    // [K slot 0, K slot 1, V slot 0, V slot 1, Q area]
+    __shared__ __attribute__((aligned(1024))) char lds[4 * TILE + QTILE];
+    char* const qarea = lds + 4 * TILE;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -177,45 +191,16 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     const int l32 = lane & 31;
     const int half = lane >> 5;
     const int role = w >> 2;                 // waves w and w+4 share a SIMD
-
-    int qb, h, b;
-    decompose(blockIdx.x, p, CAUSAL, qb, h, b);
-    const int g = h / p.rep;
-    const int q0 = qb * BM;
     const int off = p.N_k - p.N_q;           // causal diagonal offset
-    const int qw0 = q0 + w * 32;             // first row of this wave
-    const int qi = qw0 + l32;                // this lane's query row
 
-    const size_t q_row0 = (size_t)(b * p.H + h) * (size_t)p.N_q;
-    const size_t kv_row0 = (size_t)(b * p.H_kv + g) * (size_t)p.N_k;
-    const char* kbase = reinterpret_cast<const char*>(p.k + kv_row0 * D);
-    const char* vbase = reinterpret_cast<const char*>(p.v + kv_row0 * D);
-
-    int kend = p.N_k;
-    if (CAUSAL) kend = min(p.N_k, q0 + BM + off);
-    const int nkb = kend > 0 ? (kend + BN - 1) / BN : 0;
-    const int last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
-    // tiles this wave computes: a_w .. nkb_w-1.  Later tiles lie after its last
-    // row; with a sliding window ("Attention variants" §4: each row sees the W
-    // keys ending at its last causally visible key) earlier tiles lie before
-    // the window of its first row.
-    int nkb_w = nkb;
-    if (CAUSAL) nkb_w = max(0, min(nkb, (qw0 + 31 + off) / BN + 1));
-    int kb_lo = 0, a_w = 0;
-    const bool windowed = CAUSAL && p.window > 0;
-    const int first_vis = windowed ? qi + off - p.window + 1 : 0;   // first visible key of this lane's row
-    if (windowed) {
-        kb_lo = min(nkb, max(0, q0 + off - p.window + 1) / BN);
-        a_w = min(nkb_w, max(0, qw0 + off - p.window + 1) / BN);
-    }
-
-    // ---- tile loads: chunk position -> (row, global chunk)
-    int ld_voff[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int pos = i * NTHR + tid;      // 16-byte chunk position in the tile
-        const int r = pos / CPR, cp = pos % CPR;
-        ld_voff[i] = r * ROWB + swz<D>(r, cp) * 16;
+    // ---- tile loads: chunk position -> (row, global chunk).  A workgroup-wide
+    //      load covers NTHR*16/ROWB rows; the swizzle repeats every 16 rows, so
+    //      load i of a tile (or part i of the Q block) is load 0 moved by
+    //      i*NTHR*16 bytes on both sides.
+    int ld_voff;
+    {
+        const int r = tid / CPR, cp = tid % CPR;
+        ld_voff = r * ROWB + swz<D>(r, cp) * 16;
     }
     auto issue = [&](const char* base, int kb, char* dst) __attribute__((always_inline)) {
         const int key0 = kb * BN;
@@ -223,20 +208,70 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         const i32x4 rs = make_rsrc(base + (size_t)key0 * ROWB, bytes);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
-            fa_raw_buffer_load_lds(rs, (LDS_AS void*)(dst + (i * NTHR + w * 64) * 16), 16, ld_voff[i], 0, 0, 0);
+            fa_raw_buffer_load_lds(rs, (LDS_AS void*)(dst + (i * NTHR + w * 64) * 16), 16, ld_voff + i * NTHR * 16, 0,
+                                   0, 0);
     };
 
-    // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole kernel
+    // ---- work items.  Item (query block, head, batch) covers query rows
+    //      q0 .. q0+BM-1; the per-wave quantities below are set per item.
+    struct Item {
+        unsigned bh;     // b * H + h: Q, O and the LSE rows start at bh * N_q
+        unsigned bg;     // b * H_kv + h / rep: K and V rows start at bg * N_k
+        int q0;          // first query row of the block
+        int nkb;         // key tiles the block reads: kb_lo .. nkb-1
+        int kb_lo;
+    };
+    auto item_at = [&](int id) __attribute__((always_inline)) {
+        int qb, h, b;
+        decompose(id, p, CAUSAL, qb, h, b);
+        Item it;
+        it.bh = (unsigned)(b * p.H + h);
+        it.bg = (unsigned)(b * p.H_kv + h / p.rep);
+        it.q0 = qb * BM;
+        int kend = p.N_k;
+        if (CAUSAL) kend = min(p.N_k, it.q0 + BM + off);
+        it.nkb = kend > 0 ? (kend + BN - 1) / BN : 0;
+        it.kb_lo = 0;
+        // with a sliding window ("Attention variants" §4: each row sees the W
+        // keys ending at its last causally visible key) the block's first row
+        // sees nothing before its window
+        if (CAUSAL && p.window > 0) it.kb_lo = min(it.nkb, max(0, it.q0 + off - p.window + 1) / BN);
+        return it;
+    };
+    // Q block of an item into the Q area (16-byte chunks swizzled like a K
+    // tile); rows past N_q read as 0
+    auto issue_q = [&](const Item& it, int part) __attribute__((always_inline)) {
+        const unsigned bytes = (unsigned)max(0, min(BM, p.N_q - it.q0)) * ROWB;
+        const i32x4 rs = make_rsrc(p.q + ((size_t)it.bh * (size_t)p.N_q + (size_t)it.q0) * D, bytes);
+        fa_raw_buffer_load_lds(rs, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
+                               ld_voff + part * NTHR * 16, 0, 0, 0);
+    };
+
+    Item cur, nxt;
+    bool has_next;
+    int sb;                  // slot parity: tile t of the current item lives in slot (t + sb) % 2
+    int j_knext;             // period that loads the next item's first K tile
+    const char* kbase;
+    const char* vbase;
+    int qw0, qi, last_vis, first_vis, nkb_w, a_w;
+    bool windowed;
+    auto set_wave = [&]() __attribute__((always_inline)) {
+        kbase = reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D);
+        vbase = reinterpret_cast<const char*>(p.v + (size_t)cur.bg * (size_t)p.N_k * D);
+        qw0 = cur.q0 + w * 32;               // first row of this wave
+        qi = qw0 + l32;                      // this lane's query row
+        last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
+        // tiles this wave computes: a_w .. nkb_w-1.  Later tiles lie after its
+        // last row; with a window, earlier tiles lie before its first row's window
+        nkb_w = cur.nkb;
+        if (CAUSAL) nkb_w = max(0, min(cur.nkb, (qw0 + 31 + off) / BN + 1));
+        windowed = CAUSAL && p.window > 0;
+        first_vis = windowed ? qi + off - p.window + 1 : 0;   // first visible key of this lane's row
+        a_w = windowed ? min(nkb_w, max(0, qw0 + off - p.window + 1) / BN) : 0;
+    };
+
+    // ---- Q fragments (B operand of S^T = K Q^T), held for a whole item
     bf16x8 qf[KSTEPS];
-    {
-        const bool ok = qi < p.N_q;
-        const u32x4* src = reinterpret_cast<const u32x4*>(p.q + (q_row0 + (size_t)(ok ? qi : 0)) * D);
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            const u32x4 t = ok ? src[2 * ks + half] : u32x4{0, 0, 0, 0};
-            qf[ks] = __builtin_bit_cast(bf16x8, t);
-        }
-    }
 
     // ---- per-lane LDS read offsets inside a tile, computed once.  The
     //      swizzle only depends on the row modulo 16, so moving by 16 or 32 rows
@@ -263,11 +298,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     }
 
     f32x16 oacc[DBLK];
-#pragma unroll
-    for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
-    float m_run = kNegInf;      // running max (log2 units of the scaled scores)
-    float nbase = 0.f;          // -m_run, or 0 while the row has seen no key
-    float l_a = 0.f, l_b = 0.f; // this lane's part of the running sum (two chains)
+    float m_run;                // running max (log2 units of the scaled scores)
+    float nbase;                // -m_run, or 0 while the row has seen no key
+    float l_a, l_b;             // this lane's part of the running sum (two chains)
     f32x16 s[NT];               // S^T of the latest tile
     bf16x8 pf[NT][2];           // P of the latest softmax-ed tile (bf16)
 
@@ -409,20 +442,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    // ---- periods j = kb_lo .. nkb.  In period j every wave reads K tile j and
-    //      V tile j-1 only, while K tile j+1 and V tile j load into the other
-    //      slots (K tile j in K slot j%2, V tile j in V slot j%2).  The two
-    //      waves that share a SIMD run the two phases in opposite order, so one
-    //      wave's softmax overlaps the other's matrix-core work:
+    // ---- periods j = kb_lo .. nkb of an item.  In period j every wave reads
+    //      K tile j and V tile j-1 only, while K tile j+1 and V tile j load
+    //      into the other slots.  The two waves that share a SIMD run the two
+    //      phases in opposite order, so one wave's softmax overlaps the other's
+    //      matrix-core work:
     //        waves 0-3:  MFMA(PV j-1, S j), softmax(j)
     //        waves 4-7:  softmax(j-1), MFMA(PV j-1, S j)
     //      A wave computes tiles a_w .. nkb_w-1: period a_w has no PV, period
     //      nkb_w no S, and the periods outside only keep the barriers and
     //      loads.  Each role has its own loop (straight-line phases keep the
     //      register allocation tight); all waves pass the same barriers.
-    // One period: the barrier, this period's tile loads into the free slots,
-    // then the role's phases (SM: 1 = softmax of tile j-1 before the MFMAs,
-    // 2 = softmax of tile j after them).  The slot pointers are restrict
+    //      Loads for the next item ride along: one slice of its Q block per
+    //      period (the rest in the last period) and its first K tile into the
+    //      K slot that the last period leaves free.
+    // One period: the barrier, this period's loads into the free slots, then
+    // the role's phases (SM: 1 = softmax of tile j-1 before the MFMAs, 2 =
+    // softmax of tile j after them).  The slot pointers are restrict
     // qualified: within a period the loads and the LDS reads touch different
     // slots, and saying so keeps the compiler from waiting for the loads
     // before the first read (their order across periods comes from the
@@ -430,10 +466,19 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     auto period = [&](int j, auto firstc, auto lastc, auto smc, char* __restrict__ kdst, char* __restrict__ vdst,
                       const char* __restrict__ kt, const char* __restrict__ vt) __attribute__((always_inline)) {
         constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value, SM = decltype(smc)::value;
-        __builtin_amdgcn_s_waitcnt(0x0f70);                   // vmcnt(0): this wave's loads landed
+        // this wave's loads of the previous period landed (the item's first
+        // period follows the item switch, which waited already)
+        if (j != cur.kb_lo) __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
-        if (j + 1 < nkb) issue(kbase, j + 1, kdst);
-        if (j < nkb) issue(vbase, j, vdst);
+        if (j + 1 < cur.nkb) issue(kbase, j + 1, kdst);
+        else if (has_next && j == j_knext)
+            issue(reinterpret_cast<const char*>(p.k + (size_t)nxt.bg * (size_t)p.N_k * D), nxt.kb_lo, kdst);
+        if (j < cur.nkb) issue(vbase, j, vdst);
+        if (has_next) {
+            const int part_lo = min(QPARTS, j - cur.kb_lo);
+            const int part_hi = j == cur.nkb ? QPARTS : min(QPARTS, j - cur.kb_lo + 1);
+            for (int part = part_lo; part < part_hi; ++part) issue_q(nxt, part);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SM == 1) softmax_phase(j - 1);
         if constexpr (FIRST < LAST) {
@@ -445,9 +490,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         if constexpr (SM == 2) softmax_phase(j);
     };
     // slots of period j: K tile j+1 and V tile j load, K tile j and V tile j-1
-    // are read; tile t lives in slot t % 2
+    // are read
     auto run_period = [&](int j, auto firstc, auto lastc, auto smc) __attribute__((always_inline)) {
-        const int b = j & 1;
+        const int b = (j + sb) & 1;
         period(j, firstc, lastc, smc, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE, lds + b * TILE,
                lds + (2 + (b ^ 1)) * TILE);
     };
@@ -457,63 +502,138 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     using CNPV = std::integral_constant<int, NPV>;
     using CNSTEP = std::integral_constant<int, NSTEP>;
 
-    if (nkb > kb_lo) issue(kbase, kb_lo, lds + (kb_lo & 1) * TILE);
-    int j = kb_lo;
-    for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{});    // tiles before this wave's window
-    if (nkb_w > a_w) {
-        if (role == 0) {
-            run_period(j, CNPV{}, CNSTEP{}, C2{});
-            for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{});
-            run_period(j, C0{}, CNPV{}, C0{});            // j == nkb_w: PV of the last tile
-        } else {
-            run_period(j, CNPV{}, CNSTEP{}, C0{});
-            for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{});
-            run_period(j, C0{}, CNPV{}, C1{});
-        }
-        ++j;
-    }
-    for (; j <= nkb; ++j) run_period(j, C0{}, C0{}, C0{});  // tiles after this wave's rows
+    // Q fragments of the current item from the Q area (this wave's 32 rows)
+    char* const qw_lds = qarea + w * 32 * ROWB;
+    auto read_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qw_lds + k_off[ks]);
+    };
 
-    // ---- epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l).  A lane
-    //      holds 4-element pieces of one row, so storing straight from the
-    //      accumulators writes 32 rows x 8 bytes per instruction.  Instead each
-    //      wave stages its 32 x D tile in LDS (16-byte chunks XOR-swizzled by
-    //      row) and reads it back row-major: every global store is then 4 (or
-    //      8) whole rows, 1 KB contiguous.
-    float l_tot;
-    {
-        const float l_run = l_a + l_b;
-        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
-        l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-    }
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    if (p.lse && half == 0 && qi < p.N_q)
-        p.lse[q_row0 + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
-    static_assert(BM * ROWB <= 4 * TILE, "the output tile is staged in the K/V slots");
-    __syncthreads();                               // every wave is done with the K/V slots
-    char* ow = lds + w * 32 * ROWB;                // this wave's 32 rows
-#pragma unroll
-    for (int dm = 0; dm < DBLK; ++dm)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-            f32x4 t;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
-            const int c = 4 * dm + gq;             // 16-byte chunk of the row (elements 8c .. 8c+7)
-            *reinterpret_cast<bf16x4*>(ow + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
-                __builtin_convertvector(t, bf16x4);
+    // ---- the workgroup's items: round r of a persistent grid of p.grid
+    //      workgroups.  The list splits per XCD when the head count divides by
+    //      8 (list index k*8 + x is on XCD x, which runs workgroups g with
+    //      g % 8 == x); rounds walk it in alternating directions, so that a
+    //      workgroup that took a long causal block in one round takes a short
+    //      one in the next.
+    auto item_id = [&](int r) __attribute__((always_inline)) {
+        const int g = blockIdx.x;
+        if constexpr (!PERSIST) return r == 0 ? g : -1;    // one item per workgroup
+        if (((p.H * p.B) & 7) == 0) {
+            const int S = p.grid >> 3, sl = g >> 3, x = g & 7;
+            const int k = r * S + ((r & 1) ? S - 1 - sl : sl);
+            return k < (p.items >> 3) ? k * 8 + x : -1;
         }
-    constexpr int RPI = 64 / CPR;                  // rows per wave-wide 16-byte read
+        const int k = r * p.grid + ((r & 1) ? p.grid - 1 - g : g);
+        return k < p.items ? k : -1;
+    };
+
+    int r = 0;
+    int id = item_id(0);
+    if (id < 0) return;
+    cur = item_at(id);
+    sb = 0;
+    // prologue: the first item's Q block and first K tile
 #pragma unroll
-    for (int k = 0; k < 32 / RPI; ++k) {
-        const int r = k * RPI + lane / CPR, c = lane % CPR;
-        const u32x4 t = *reinterpret_cast<const u32x4*>(ow + r * ROWB + ((c ^ (r & (CPR - 1))) * 16));
-        if (qw0 + r < p.N_q)
-            *reinterpret_cast<u32x4*>(p.o + (q_row0 + qw0 + r) * D + c * 8) = t;
+    for (int part = 0; part < QPARTS; ++part) issue_q(cur, part);
+    if (cur.nkb > cur.kb_lo)
+        issue(reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D), cur.kb_lo, lds + (cur.kb_lo & 1) * TILE);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+    read_q();
+
+    for (;;) {
+        const int nid = item_id(r + 1);
+        has_next = PERSIST && nid >= 0;
+        nxt = has_next ? item_at(nid) : cur;
+        j_knext = max(cur.kb_lo, cur.nkb - 1);
+        set_wave();
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
+        m_run = kNegInf;
+        nbase = 0.f;
+        l_a = 0.f;
+        l_b = 0.f;
+
+        int j = cur.kb_lo;
+        for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{});    // tiles before this wave's window
+        if (nkb_w > a_w) {
+            if (role == 0) {
+                run_period(j, CNPV{}, CNSTEP{}, C2{});
+                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{});
+                run_period(j, C0{}, CNPV{}, C0{});            // j == nkb_w: PV of the last tile
+            } else {
+                run_period(j, CNPV{}, CNSTEP{}, C0{});
+                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{});
+                run_period(j, C0{}, CNPV{}, C1{});
+            }
+            ++j;
+        }
+        for (; j <= cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{});  // tiles after this wave's rows
+
+        // ---- item switch: the next item's Q block and first K tile landed and
+        //      every wave is done with this item's slots
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+        // epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l).  A lane
+        // holds 4-element pieces of one row, so storing straight from the
+        // accumulators would write 32 rows x 8 bytes per instruction.  Each
+        // wave stages its 32 x D tile in its own 32 rows of the Q area (after
+        // taking the next item's Q fragments from there; 16-byte chunks
+        // XOR-swizzled by row) and reads it back row-major: every global store
+        // is then 4 (or 8) whole rows, 1 KB contiguous.
+        float l_tot;
+        {
+            const float l_run = l_a + l_b;
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_run), __float_as_uint(l_run), false, false);
+            l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        }
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+        if (p.lse && half == 0 && qi < p.N_q)
+            p.lse[(size_t)cur.bh * (size_t)p.N_q + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
+        if (has_next) read_q();
+#pragma unroll
+        for (int dm = 0; dm < DBLK; ++dm)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+                f32x4 t;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
+                const int c = 4 * dm + gq;             // 16-byte chunk of the row (elements 8c .. 8c+7)
+                *reinterpret_cast<bf16x4*>(qw_lds + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
+                    __builtin_convertvector(t, bf16x4);
+            }
+        constexpr int RPI = 64 / CPR;                  // rows per wave-wide 16-byte read
+#pragma unroll
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int rr = k * RPI + lane / CPR, c = lane % CPR;
+            const u32x4 t = *reinterpret_cast<const u32x4*>(qw_lds + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
+            if (qw0 + rr < p.N_q)
+                *reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8) = t;
+        }
+        if (!has_next) break;
+        sb = (j_knext + 1 + sb - nxt.kb_lo) & 1;   // the next item's first K tile sits in slot (j_knext + 1 + sb) % 2
+        cur = nxt;
+        ++r;
     }
 }
 
-template <int D, int NW, bool CAUSAL>
+// Workgroups that fit on the device at once (cached per device): the grid of
+// the persistent kernel.
+template <typename K>
+int resident_blocks(K kernel, int threads)
+{
+    static int cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cache[dev] > 0) return cache[dev];
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
+    return cache[dev];
+}
+
+template <int D, int NW, bool CAUSAL, bool PERSIST>
 hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
@@ -535,9 +655,19 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     // scale 0 runs as a tiny positive scale: every exp2 argument then rounds to
     // 0 exactly as with scale 0, and masked scores stay -inf instead of NaN
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
-    const long long blocks = (long long)p.nqb * a.H * a.B;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL>), dim3((unsigned)blocks), dim3(NW * 64), 0, stream, p);
+    const long long items = (long long)p.nqb * a.H * a.B;
+    if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    if (items == 0) return hipSuccess;
+    long long grid = items;
+    if (PERSIST) {
+        const int resident = resident_blocks(fwd_bf16_kernel<D, NW, CAUSAL, PERSIST>, NW * 64);
+        if (resident <= 0) return hipErrorInvalidDevice;
+        if (resident < grid) grid = resident;
+        if (((a.H * a.B) & 7) == 0) grid = grid / 8 * 8;   // whole XCD rows (items is a multiple of 8)
+    }
+    p.items = (int)items;
+    p.grid = (int)grid;
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, PERSIST>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -550,10 +680,13 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream)
 {
     const int group = FA_FWD_GROUP;
+    // d = 128 runs persistent (one workgroup per CU, item switches hidden
+    // behind the next item's loads); d = 64 fits two workgroups per CU, which
+    // hide each other's start and end, and runs one item per workgroup
     if (a.d == 128)
-        return a.causal ? launch<128, 8, true>(a, group, stream) : launch<128, 8, false>(a, group, stream);
+        return a.causal ? launch<128, 8, true, true>(a, group, stream) : launch<128, 8, false, true>(a, group, stream);
     if (a.d == 64)
-        return a.causal ? launch<64, 8, true>(a, group, stream) : launch<64, 8, false>(a, group, stream);
+        return a.causal ? launch<64, 8, true, false>(a, group, stream) : launch<64, 8, false, false>(a, group, stream);
     return hipErrorInvalidValue;
 }
 
