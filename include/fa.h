@@ -111,6 +111,20 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                        float scale, int causal, hipStream_t stream);
 
 /*
+ * fa_fwd_set_max_workgroups -- a cap on the workgroups of the bf16 prefill
+ * at d = 128 (fa_fwd, fa_fwd_window).  That kernel runs a persistent grid,
+ * one workgroup per slot that fits on the device, each working through a
+ * list of (query block, head, batch) items; the cap leaves compute units to
+ * other work on the device, and a small cap makes every workgroup run many
+ * items in a row.  It is a scheduling control, not part of the operation:
+ * results are the same for every value.
+ *   n = 0: no cap (the default); n >= 1: at most n workgroups.
+ *   n < 0: FA_ERR_INVALID_ARGUMENT.
+ * The setting is process-wide and applies to launches issued after the call.
+ */
+fa_status_t fa_fwd_set_max_workgroups(int n);
+
+/*
  * fa_decode_workspace_bytes -- size of the workspace fa_decode needs:
  * fp32 partial outputs [B,H,num_splits,d] followed by fp32 partial
  * log-sum-exps [B,H,num_splits].  Returns 0 for invalid arguments.

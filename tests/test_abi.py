@@ -187,3 +187,14 @@ def test_decode_fp8_rejects_before_launch(lib, name, change, expect):
     st = lib.fa_decode_fp8(a["q"], a["k"], a["v"], 0.5, 0.5, a["lens"], a["o"], a["lse"], a["B"], a["H"],
                            a["H_kv"], a["N_max"], a["d"], a["scale"], a["S"], a["ws"], a["ws_bytes"], None)
     assert st == expect, (name, st, lib.fa_last_error())
+
+
+@pytest.mark.parametrize("n", [-1, -100])
+def test_fwd_max_workgroups_rejects_negative(lib, n):
+    assert lib.fa_fwd_set_max_workgroups(n) == INVALID
+    assert b"n must be >= 0" in lib.fa_last_error()
+
+
+def test_fwd_max_workgroups_accepts_caps(lib):
+    for n in (5, 1, 0):          # ends at 0: no cap for the rest of the session
+        assert lib.fa_fwd_set_max_workgroups(n) == api.FA_OK

@@ -256,6 +256,49 @@ def test_decode_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+# ------------------------------------------------------------------ persistent prefill grid
+# A cap on the workgroups makes every workgroup of the persistent d=128 kernel
+# run many items in a row (item switches, the next item's Q and first K tile
+# loaded during the current one, slot parity carried across items), at sizes
+# the oracle checks element by element.
+PERSIST_CASES = [
+    # B, H, H_kv, N_q, N_k, d, causal, window
+    (2, 8, 2, 600, 600, 128, True, None),      # 48 items; per-XCD list at caps >= 8
+    (1, 3, 1, 700, 700, 128, False, None),     # 9 items; whole-list rounds
+    (1, 8, 2, 900, 900, 128, True, 70),        # window: first tile parity changes between items
+    (1, 8, 1, 900, 300, 128, True, None),      # N_q > N_k: items whose rows see no key
+    (2, 4, 4, 300, 1000, 128, True, None),     # N_q < N_k
+    (1, 4, 2, 517, 517, 64, True, None),       # d = 64 runs one item per workgroup: cap has no effect
+]
+
+
+@pytest.fixture
+def _grid_cap():
+    yield
+    api.fwd_set_max_workgroups(0)
+
+
+@pytest.mark.parametrize("cap", [1, 3, 8, 13])
+@pytest.mark.parametrize("case", PERSIST_CASES, ids=lambda c: "x".join(str(x) for x in c))
+def test_fwd_persistent_rounds(case, cap, _grid_cap):
+    import torch
+    B, H, H_kv, N_q, N_k, d, causal, window = case
+    spec = _spec(B, H, H_kv, N_q, N_k, d, causal, seed=31)
+    say(f"fa_fwd persistent cap={cap} {spec.name} window={window}")
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    api.fwd_set_max_workgroups(cap)
+    o, lse = api.fwd(q, k, v, causal=causal, scale=spec.scale, window=window)
+    torch.cuda.synchronize()
+    api.fwd_set_max_workgroups(0)
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, causal, window=window)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"cap {cap}")
+    # the same launch without a cap gives the same bits
+    o2, lse2 = api.fwd(q, k, v, causal=causal, scale=spec.scale, window=window)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+
+
 # ------------------------------------------------------------------ sliding window
 WINDOW_BF16 = [
     # B, H, H_kv, N_q, N_k, d, window

@@ -23,8 +23,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode", "fa_decode_window", "fa_decode_paged",
-            "fa_decode_fp8", "fa_decode_workspace_bytes", "fa_status_string", "fa_last_error")
+EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_fwd_set_max_workgroups", "fa_decode",
+            "fa_decode_window", "fa_decode_paged", "fa_decode_fp8", "fa_decode_workspace_bytes",
+            "fa_status_string", "fa_last_error")
 
 _lib = None
 
@@ -62,6 +63,8 @@ def load():
     lib.fa_decode_paged.restype = i
     lib.fa_decode_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode_fp8.restype = i
+    lib.fa_fwd_set_max_workgroups.argtypes = [i]
+    lib.fa_fwd_set_max_workgroups.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -155,6 +158,11 @@ def fwd_f32(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     """fa_fwd_f32: the same with fp32 tensors."""
     torch = _torch()
     return _fwd(load().fa_fwd_f32, torch.float32, q, k, v, causal, scale, out, lse)
+
+
+def fwd_set_max_workgroups(n: int) -> None:
+    """fa_fwd_set_max_workgroups: cap the persistent prefill grid (0 = no cap)."""
+    check(load().fa_fwd_set_max_workgroups(int(n)))
 
 
 def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:

@@ -4,6 +4,7 @@
 #include "fa.h"
 #include "fa_internal.h"
 
+#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -12,6 +13,9 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+
+// cap on the persistent prefill grid (fa_fwd_set_max_workgroups), 0 = none
+std::atomic<int> g_fwd_max_workgroups{0};
 
 fa_status_t fail(fa_status_t s, const char* fmt, ...)
 {
@@ -130,6 +134,7 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
     fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
     if (s != FA_OK) return s;
     fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0, 0};
+    a.max_workgroups = g_fwd_max_workgroups.load(std::memory_order_relaxed);
     return from_hip(fa::launch_fwd_bf16(a, stream), "fa_fwd launch");
 }
 
@@ -142,7 +147,15 @@ fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, 
     if (window < 1)
         return fail(FA_ERR_INVALID_ARGUMENT, "window=%d must be at least 1", window);
     fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, 1, window};
+    a.max_workgroups = g_fwd_max_workgroups.load(std::memory_order_relaxed);
     return from_hip(fa::launch_fwd_bf16(a, stream), "fa_fwd_window launch");
+}
+
+fa_status_t fa_fwd_set_max_workgroups(int n)
+{
+    if (n < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_set_max_workgroups: n must be >= 0");
+    g_fwd_max_workgroups.store(n, std::memory_order_relaxed);
+    return FA_OK;
 }
 
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,

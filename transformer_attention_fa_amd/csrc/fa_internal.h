@@ -19,6 +19,7 @@ struct FwdArgs {
     float scale;         // softmax scale on q.k
     int causal;
     int window;          // sliding window in keys (causal only), 0 = none
+    int max_workgroups = 0;   // cap on the persistent grid, 0 = none
 };
 
 // One decode step, as validated by fa_decode.

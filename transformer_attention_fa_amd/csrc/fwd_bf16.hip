@@ -101,6 +101,7 @@ struct Params {
     int group;    // heads per longest-first group of the item order
     int items;    // work items (query blocks x heads x batch)
     int grid;     // workgroups of the persistent grid
+    int xcd;      // 1: the item list and the grid split per XCD (both multiples of 8)
     float c;      // scale * log2(e), > 0
 };
 
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     auto item_id = [&](int r) __attribute__((always_inline)) {
         const int g = blockIdx.x;
         if constexpr (!PERSIST) return r == 0 ? g : -1;    // one item per workgroup
-        if (((p.H * p.B) & 7) == 0) {
+        if (p.xcd) {
             const int S = p.grid >> 3, sl = g >> 3, x = g & 7;
             const int k = r * S + ((r & 1) ? S - 1 - sl : sl);
             return k < (p.items >> 3) ? k * 8 + x : -1;
@@ -659,12 +660,20 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     if (items == 0) return hipSuccess;
     long long grid = items;
+    int xcd = 0;
     if (PERSIST) {
         const int resident = resident_blocks(fwd_bf16_kernel<D, NW, CAUSAL, PERSIST>, NW * 64);
         if (resident <= 0) return hipErrorInvalidDevice;
         if (resident < grid) grid = resident;
-        if (((a.H * a.B) & 7) == 0) grid = grid / 8 * 8;   // whole XCD rows (items is a multiple of 8)
+        if (a.max_workgroups > 0 && a.max_workgroups < grid) grid = a.max_workgroups;
+        // the per-XCD split needs whole rows of 8 workgroups (items is then a
+        // multiple of 8 too); otherwise the rounds walk the whole list
+        if (((a.H * a.B) & 7) == 0 && grid >= 8) {
+            grid = grid / 8 * 8;
+            xcd = 1;
+        }
     }
+    p.xcd = xcd;
     p.items = (int)items;
     p.grid = (int)grid;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, PERSIST>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p);
