@@ -1,7 +1,7 @@
 // fwd_bf16.hip -- tiled exact attention forward on gfx950 bf16 MFMA.
 //
 // Method ("Attention variants: GQA/MQA/FlashAttention" (youngju.dev) §3):
-// cut Q into blocks (one per workgroup) and K/V into blocks streamed through
+// cut Q into blocks (one per work item) and K/V into blocks streamed through
 // LDS; per query row keep a running maximum m and running sum l; for each key
 // block compute the block scores, bring the accumulator and l to a new m when
 // needed, add the block's exp(S - m) V; divide by l at the end.  Causal
@@ -11,13 +11,14 @@
 // (toolsku.com) GQA code).
 //
 // gfx950 mapping (not from the pages, whose kernel targets other GPUs):
-//  * persistent grid: one workgroup per resident slot (256 CUs x 1 on
-//    MI355X), each working through a list of items (query block of BM = 256
-//    rows, head, batch); workgroup = 8 waves, each wave owns 32 rows of the
-//    block; two waves share each SIMD;
+//  * work item = (query block of BM = 256 rows, head, batch); workgroup = 8
+//    waves, each wave owns 32 rows of the block; two waves share each SIMD.
+//    At d = 128 the grid is persistent: one workgroup per resident slot
+//    (256 CUs x 1 on MI355X), each working through a list of items; d = 64
+//    fits two workgroups per CU and runs one item per workgroup;
 //  * scores are computed transposed, S^T = K Q^T, on v_mfma_f32_32x32x16_bf16
 //    (A = K fragment from LDS, B = Q fragment held in VGPRs for the whole
-//    kernel).  In the 32x32 accumulator layout lane l holds column l%32 -- one
+//    item).  In the 32x32 accumulator layout lane l holds column l%32 -- one
 //    query row -- and 16 of the 32 keys, so row max and row sum are in-lane
 //    plus one exchange with lane l^32 (v_permlane32_swap);
 //  * the output is accumulated transposed too, O^T += V^T P^T, so it shares
@@ -58,6 +59,7 @@
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -618,20 +620,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     }
 }
 
-// Workgroups that fit on the device at once (cached per device): the grid of
-// the persistent kernel.
+// Workgroups that fit on the current device at once: the grid of the
+// persistent kernel.  Cached per device and kernel (host threads may race to
+// fill an entry; they store the same value).
 template <typename K>
 int resident_blocks(K kernel, int threads)
 {
-    static int cache[64];
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cache[dev] > 0) return cache[dev];
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
-    cache[dev] = cus * (per_cu > 0 ? per_cu : 1);
-    return cache[dev];
+    const int n = cus * (per_cu > 0 ? per_cu : 1);
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
 }
 
 template <int D, int NW, bool CAUSAL, bool PERSIST>
