@@ -108,6 +108,19 @@ __device__ __forceinline__ int dswz(int r, int c)
     else return c ^ (2 * ((r >> 1) & 3) + ((r >> 3) & 1));
 }
 
+// Position of 16-byte chunk c of row r (0..15) of a 16-key bf16 K tile (and
+// of the staged Q rows, read the same way).  The K fragment read -- 16 rows,
+// one chunk per row for each 16 lanes -- measures 2-way bank conflicts on
+// gfx950 with dswz's layout and none with chunk XOR row at d = 128 (the
+// transposing V reads show the opposite), so the K and V tiles are laid out
+// differently.
+template <int D>
+__device__ __forceinline__ int kswz(int r, int c)
+{
+    if constexpr (D == 128) return c ^ (r & 15);
+    else return dswz<D>(r, c);
+}
+
 // Position of 16-byte chunk c of row r (0..15) of a 16-key FP8 tile (rows of D
 // bytes).  Conflict free for the 8-byte K fragment reads (16 rows, the two
 // halves of one chunk per row pair of lanes) on the 64-bank LDS.
@@ -226,7 +239,7 @@ __device__ __forceinline__ int sequence_for(const SplitParams& p, int z)
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-// KS 8-byte LDS reads (FP8 K fragments), waiting for their own results
+// N 8-byte LDS reads (FP8 K fragments, FP8 V codes), waiting for their own results
 template <int N>
 __device__ __forceinline__ void lds_read_b64n(u32x2 (&a)[N], const unsigned (&p)[N])
 {
@@ -241,18 +254,6 @@ __device__ __forceinline__ void lds_read_b64n(u32x2 (&a)[N], const unsigned (&p)
                      : "=&v"(a[0]), "=&v"(a[1])
                      : "v"(p[0]), "v"(p[1])
                      : "memory");
-}
-// N 16-byte LDS reads, waiting for their own results
-template <int N>
-__device__ __forceinline__ void lds_read_b128n(u32x4 (&a)[N], const unsigned (&p)[N])
-{
-    if constexpr (N == 2)
-        asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
-                     : "=&v"(a[0]), "=&v"(a[1])
-                     : "v"(p[0]), "v"(p[1])
-                     : "memory");
-    else
-        asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(a[0]) : "v"(p[0]) : "memory");
 }
 // N 16-byte LDS writes, complete before the block ends
 template <int N>
@@ -323,12 +324,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     const char* vbase = p.v + kv_row0 * ROWB;
     char* wl = lds + w * WAVE_LDS;
 
-    int ld_off[LOADS];
+    int ld_k[LOADS], ld_v[LOADS];
 #pragma unroll
     for (int i = 0; i < LOADS; ++i) {
         const int pos = i * 64 + lane;
         const int r = pos / CPR, cp = pos % CPR;
-        ld_off[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : dswz<D>(r, cp)) * 16;
+        ld_k[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : kswz<D>(r, cp)) * 16;
+        ld_v[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : dswz<D>(r, cp)) * 16;
     }
     // tile t of the chunk into stage s: rows past the chunk read as 0
     auto issue = [&](int t, int s) __attribute__((always_inline)) {
@@ -348,8 +350,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         char* dst = wl + s * 2 * TILEB;
 #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_off[i], 0, 0, kStreamPolicy);
-            fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_off[i], 0, 0, kStreamPolicy);
+            fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_k[i], 0, 0, kStreamPolicy);
+            fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_v[i], 0, 0, kStreamPolicy);
         }
     };
 
@@ -360,7 +362,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         if constexpr (KV8)     // 8 bytes: d = 32*ks + 8*g4 .. +8 = half (g4 & 1) of chunk 2*ks + g4/2
             k_off[ks] = l16 * ROWB + fswz<D>(l16, 2 * ks + (g4 >> 1)) * 16 + (g4 & 1) * 8;
         else
-            k_off[ks] = l16 * ROWB + dswz<D>(l16, 4 * ks + g4) * 16;
+            k_off[ks] = l16 * ROWB + kswz<D>(l16, 4 * ks + g4) * 16;
     }
     // V^T fragments through transposing reads of a bf16 tile: the V tile of the
     // stage, or (FP8) the wave's bf16 copy of it
@@ -372,15 +374,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
             v_off[dm] = (KV8 ? VSTAGE : TILEB) + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 +
                         (l16 & 1) * 8;
     }
-    // FP8: lane l converts row l/4 of the V tile, d = (l%4)*D/4 .. +D/4
-    constexpr int CV = D / 64;               // 16-byte FP8 chunks per lane
-    unsigned cv_src[CV], cv_dst[2 * CV];
+    // FP8: write i of lane l fills bytes 1024*i + 16*l of the wave's bf16 copy
+    // of the V tile (a linear write, free of bank conflicts); that position
+    // holds bf16 chunk dswz(row, position) of its row, whose 8 FP8 codes the
+    // lane reads first (one 8-byte read)
+    constexpr int NCV = TK * D * 2 / 1024;   // 16-byte writes per lane per tile
+    unsigned cv_src[NCV], cv_dst[NCV];
     if constexpr (KV8) {
-        const int r = lane >> 2, part = lane & 3;
 #pragma unroll
-        for (int i = 0; i < CV; ++i) cv_src[i] = TILEB + r * ROWB + fswz<D>(r, part * CV + i) * 16;
-#pragma unroll
-        for (int i = 0; i < 2 * CV; ++i) cv_dst[i] = VSTAGE + r * QROWB + dswz<D>(r, part * 2 * CV + i) * 16;
+        for (int i = 0; i < NCV; ++i) {
+            const int byte = i * 1024 + lane * 16;
+            const int r = byte / QROWB, cc = dswz<D>(r, (byte % QROWB) / 16);
+            cv_dst[i] = VSTAGE + byte;
+            cv_src[i] = TILEB + r * ROWB + fswz<D>(r, cc >> 1) * 16 + (cc & 1) * 8;
+        }
     }
 
     f32x4 oacc[DB];
@@ -389,11 +396,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     float m_run = kNegInf, nbase = 0.f, l_run = 0.f;
 
     // ---- Q rows of the group into LDS (one 1 KB slice per wave; rows past the
-    // group read as 0), then the first two tiles of this wave
+    // group read as 0; 16-byte chunks placed like a K tile row, whose fragment
+    // reads they repeat), then the first two tiles of this wave
     char* qs = lds + NW * WAVE_LDS;
     {
+        const int pos = w * 64 + lane;                  // 16-byte chunk position in the Q block
+        const int qr = pos / (QROWB / 16), qc = pos % (QROWB / 16);
         const i32x4 rq = make_rsrc(p.q + ((size_t)b * p.H + h0) * D, (unsigned)nh * QROWB);
-        fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, w * 1024 + lane * 16, 0, 0, 0);
+        fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, qr * QROWB + kswz<D>(qr, qc) * 16, 0, 0, 0);
     }
     if (nt_w > 0) issue(w, 0);
     if (nt_w > 1) issue(w + NW, 1);
@@ -401,12 +411,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     else if (nt_w > 0) wait_vmcnt<2 * LOADS>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();               // every wave waited for its own slice
-    // Q^T fragments (B of S^T): head l16, d = 32*ks + 8*g4 .. +8
+    // Q^T fragments (B of S^T): head l16, d = 32*ks + 8*g4 .. +8 (chunk 4*ks + g4)
     bf16x8 qf[KS];
     {
-        const unsigned qa = (unsigned)(uintptr_t)(LDS_AS char*)qs + l16 * QROWB + g4 * 16;
-        if constexpr (KS == 4) lds_read_k4(qf, qa, qa + 64, qa + 128, qa + 192);
-        else lds_read_k2(qf, qa, qa + 64);
+        const unsigned qa = (unsigned)(uintptr_t)(LDS_AS char*)qs + l16 * QROWB;
+        if constexpr (KS == 4)
+            lds_read_k4(qf, qa + kswz<D>(l16, g4) * 16, qa + kswz<D>(l16, 4 + g4) * 16, qa + kswz<D>(l16, 8 + g4) * 16,
+                        qa + kswz<D>(l16, 12 + g4) * 16);
+        else lds_read_k2(qf, qa + kswz<D>(l16, g4) * 16, qa + kswz<D>(l16, 4 + g4) * 16);
     }
 
     const unsigned wl_addr = (unsigned)(uintptr_t)(LDS_AS char*)wl;
@@ -426,21 +438,21 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
                                                            (unsigned)(hi >> 32)}));
             }
             // V tile: FP8 codes -> the wave's bf16 copy, laid out like a bf16 tile
-            unsigned va[CV], wa[2 * CV];
+            unsigned va[NCV], wa[NCV];
 #pragma unroll
-            for (int i = 0; i < CV; ++i) va[i] = st + cv_src[i];
+            for (int i = 0; i < NCV; ++i) {
+                va[i] = st + cv_src[i];
+                wa[i] = wl_addr + cv_dst[i];
+            }
+            u32x2 v8[NCV];
+            u32x4 vb[NCV];
+            lds_read_b64n<NCV>(v8, va);
 #pragma unroll
-            for (int i = 0; i < 2 * CV; ++i) wa[i] = wl_addr + cv_dst[i];
-            u32x4 v8[CV], vb[2 * CV];
-            lds_read_b128n<CV>(v8, va);
-#pragma unroll
-            for (int i = 0; i < CV; ++i)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const unsigned long long a = e4m3x4_to_bf16x4(v8[i][2 * h]), c2 = e4m3x4_to_bf16x4(v8[i][2 * h + 1]);
-                    vb[2 * i + h] = u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)c2, (unsigned)(c2 >> 32)};
-                }
-            lds_write_b128n<2 * CV>(wa, vb);
+            for (int i = 0; i < NCV; ++i) {
+                const unsigned long long a = e4m3x4_to_bf16x4(v8[i][0]), c2 = e4m3x4_to_bf16x4(v8[i][1]);
+                vb[i] = u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)c2, (unsigned)(c2 >> 32)};
+            }
+            lds_write_b128n<NCV>(wa, vb);
         } else {
             if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
             else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
@@ -498,10 +510,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         sh_m[w * 16 + l16] = m_run;
         sh_l[w * 16 + l16] = l_head;
     }
+    // row (w, head l16): the 4 accumulator values of d-block dm are 16
+    // contiguous bytes, chunk 4*dm + g4 of the row; the chunk index is XORed
+    // with the head so the 16 heads of one write land in different banks
 #pragma unroll
     for (int dm = 0; dm < DB; ++dm)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sh_o[(w * 16 + l16) * D + dm * 16 + 4 * g4 + r] = oacc[dm][r];
+        *reinterpret_cast<f32x4*>(sh_o + (w * 16 + l16) * D + (((4 * dm + g4) ^ l16) << 2)) = oacc[dm];
     __syncthreads();
     for (int e = tid; e < nh * D; e += 256) {
         const int hh = e / D, d = e % D;
@@ -515,7 +529,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
             const float mw = sh_m[ww * 16 + hh];
             const float a = (mw == kNegInf) ? 0.f : fast_exp2(mw - base);
             ll += a * sh_l[ww * 16 + hh];
-            oo += a * sh_o[(ww * 16 + hh) * D + d];
+            oo += a * sh_o[(ww * 16 + hh) * D + ((((d >> 2) ^ hh)) << 2) + (d & 3)];
         }
         const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
         p.part_o[row * D + d] = ll > 0.f ? oo / ll * p.v_scale : 0.f;
