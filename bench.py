@@ -52,8 +52,8 @@ def kernel_source_hash(files):
     return h.hexdigest()[:16]
 
 
-def traffic_for(kernel_key, src_files):
-    """HBM traffic per launch from committed rocprofv3 --pmc summaries, or None
+def counter_record(kernel_key, src_files):
+    """The committed rocprofv3 --pmc figures for a kernel and workload, or None
     when the kernel source changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -64,7 +64,24 @@ def traffic_for(kernel_key, src_files):
         return None
     if not rec or rec.get("source_hash") != kernel_source_hash(src_files):
         return None
-    return rec.get("bytes_per_launch")
+    return rec
+
+
+def traffic_for(kernel_key, src_files):
+    """HBM traffic per launch (FETCH_SIZE + WRITE_SIZE, calibrated), or None."""
+    rec = counter_record(kernel_key, src_files)
+    return rec.get("bytes_per_launch") if rec else None
+
+
+def counters_for(kernel_key, src_files):
+    """Matrix-core busy fraction and LDS bank-conflict fraction from the
+    committed counter runs, or None."""
+    rec = counter_record(kernel_key, src_files)
+    if not rec:
+        return None
+    out = {k: round(v, 4) for k, v in rec.items()
+           if k.startswith("mfma_busy") or k.startswith("lds_bank_conflict") or k == "counter_clock_ghz"}
+    return out or None
 
 
 def cpu_baseline(spec, n_batches):
@@ -199,12 +216,14 @@ def add_rooflines(nxt):
         if r["unit"] == "TFLOP/s":
             r["roofline"] = {"bound": "mfma", "achieved": r["value"], "peak": roofline.PEAK_BF16_TFLOPS,
                              "unit": "TFLOP/s", "frac": r["value"] / roofline.PEAK_BF16_TFLOPS,
-                             "traffic": traffic_for(f"fwd_bf16:{name}", ["fwd_bf16.hip"]), "kernel": "fwd_bf16_kernel"}
+                             "traffic": traffic_for(f"fwd_bf16:{name}", ["fwd_bf16.hip"]), "kernel": "fwd_bf16_kernel",
+                             "counters": counters_for(f"fwd_bf16:{name}", ["fwd_bf16.hip"])}
         else:
             r["roofline"] = {"bound": "hbm", "achieved": r["value"], "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
                              "frac": r["value"] / roofline.PEAK_HBM_GBPS,
                              "traffic": traffic_for(f"decode:{name}", ["decode.hip"]),
-                             "kernel": "decode_split_kernel + decode_combine_kernel"}
+                             "kernel": "decode_split_kernel + decode_combine_kernel",
+                             "counters": counters_for(f"decode:{name}", ["decode.hip"])}
     return nxt
 
 
@@ -303,7 +322,8 @@ def main():
                            "unit": "TFLOP/s", "frac": tflops / roofline.PEAK_BF16_TFLOPS, "traffic": traffic,
                            "kernel": "fwd_bf16_kernel", "launch_ms_avg": t_avg,
                            "launch_ms_median": float(np.median(t_pf)), "launch_ms_min": float(np.min(t_pf)),
-                           "flop_per_launch": flops}
+                           "flop_per_launch": flops,
+                           "counters": counters_for(f"fwd_bf16:{pspec.name}", ["fwd_bf16.hip"])}
         config["workload"] = pspec.name
         config["prefill"] = {"B": pspec.B, "H": pspec.H, "H_kv": pspec.H_kv, "N_q": pspec.N_q, "N_k": pspec.N_k,
                              "d": pspec.d, "causal": pspec.causal, "seed": pspec.seed}
@@ -318,7 +338,8 @@ def main():
                          "roofline": {"bound": "hbm", "achieved": gbps, "peak": roofline.PEAK_HBM_GBPS,
                                       "unit": "GB/s", "frac": gbps / roofline.PEAK_HBM_GBPS,
                                       "traffic": traffic_for(f"decode:{dspec.name}", ["decode.hip"]),
-                                      "kernel": "decode_split_kernel + decode_combine_kernel"}}
+                                      "kernel": "decode_split_kernel + decode_combine_kernel",
+                                      "counters": counters_for(f"decode:{dspec.name}", ["decode.hip"])}}
         config["workload"] = (config["workload"] + " + " if config["workload"] else "") + dspec.name
         config["decode"] = {"B": dspec.B, "H": dspec.H, "H_kv": dspec.H_kv, "d": dspec.d,
                             "seq_len_range": [dspec.len_lo, dspec.len_hi], "num_splits": dspec.num_splits,
