@@ -521,3 +521,56 @@ def test_decode_fp8_workload_full_compare():
     o_ref, lse_ref = oracle.decode_fp8(data.q, data.k_cache, data.v_cache, spec.k_scale, spec.v_scale,
                                        data.seq_lens, spec.scale)
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
+# ------------------------------------------------------------------ HIP graph capture
+def test_hip_graph_capture_replays_match_eager():
+    """A prefill call and a decode step captured in one HIP graph (through
+    torch.cuda.graph, on the capture stream the binding passes down) replay
+    to the eager results bit for bit, replay after replay, with other eager
+    work between the replays.  The library allocates, clears and syncs
+    nothing on the call path, so nothing else needs to be captured."""
+    import torch
+    pspec = _spec(1, 4, 2, 300, 300, 128, True, seed=41)
+    pd = inputs.prefill_inputs(pspec)
+    q, k, v = (bf16_to_device(x) for x in (pd.q, pd.k, pd.v))
+    dspec = inputs.Decode("graph_decode", 2, 8, 2, 128, 1, 700, 700, 4, 43)
+    dd = inputs.decode_inputs(dspec)
+    dq, kc, vc = (bf16_to_device(x) for x in (dd.q, dd.k_cache, dd.v_cache))
+    lens = torch.from_numpy(dd.seq_lens).to("cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+    do = torch.empty_like(dq)
+    dl = torch.empty(dq.shape[:-1], dtype=torch.float32, device="cuda")
+    ws = torch.empty(api.decode_workspace_bytes(2, 8, 128, 4), dtype=torch.uint8, device="cuda")
+
+    def step():
+        api.fwd(q, k, v, causal=True, scale=pspec.scale, out=o, lse=lse)
+        api.decode(dq, kc, vc, lens, num_splits=4, scale=dspec.scale, out=do, lse=dl, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (o, lse, do, dl)]
+    o_ref, lse_ref = oracle.attention(pd.q, pd.k, pd.v, pspec.scale, True)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label="eager prefill")
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    other = torch.randn(1, 4, 300, 128, device="cuda").to(torch.bfloat16)
+    for rep in range(4):
+        for t in (o, lse, do, dl):
+            t.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((o, lse, do, dl), ref):
+            assert torch.equal(got.view(torch.int16) if got.dtype == torch.bfloat16 else got.view(torch.int32),
+                               want.view(torch.int16) if want.dtype == torch.bfloat16 else want.view(torch.int32)), rep
+        # eager work between replays, on other buffers
+        api.fwd(other, k, v, causal=True, scale=pspec.scale)
+        torch.cuda.synchronize()
