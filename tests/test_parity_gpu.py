@@ -574,3 +574,39 @@ def test_hip_graph_capture_replays_match_eager():
         # eager work between replays, on other buffers
         api.fwd(other, k, v, causal=True, scale=pspec.scale)
         torch.cuda.synchronize()
+
+
+def test_concurrent_streams_match_sequential():
+    """A persistent prefill launch and a decode step in flight together on two
+    streams (plus a second prefill on a third) give the same bits as when run
+    one at a time: the kernels keep no state between or across launches."""
+    import torch
+    torch.manual_seed(47)
+    q = torch.randn(2, 8, 1500, 128, device="cuda").to(torch.bfloat16)
+    k = torch.randn(2, 2, 1500, 128, device="cuda").to(torch.bfloat16)
+    v = torch.randn(2, 2, 1500, 128, device="cuda").to(torch.bfloat16)
+    q2 = torch.randn(1, 4, 900, 64, device="cuda").to(torch.bfloat16)
+    k2 = torch.randn(1, 4, 900, 64, device="cuda").to(torch.bfloat16)
+    v2 = torch.randn(1, 4, 900, 64, device="cuda").to(torch.bfloat16)
+    dspec = inputs.Decode("streams_decode", 4, 16, 4, 128, 1, 3000, 9000, 8, 53)
+    dd = inputs.decode_inputs(dspec)
+    dq, kc, vc = (bf16_to_device(x) for x in (dd.q, dd.k_cache, dd.v_cache))
+    lens = torch.from_numpy(dd.seq_lens).to("cuda")
+    o_a, l_a = api.fwd(q, k, v, causal=True)
+    o_b, l_b = api.fwd(q2, k2, v2, causal=False)
+    do_a, dl_a = api.decode(dq, kc, vc, lens, num_splits=8)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        with torch.cuda.stream(streams[0]):
+            o1, l1 = api.fwd(q, k, v, causal=True)
+        with torch.cuda.stream(streams[1]):
+            do1, dl1 = api.decode(dq, kc, vc, lens, num_splits=8)
+        with torch.cuda.stream(streams[2]):
+            o2, l2 = api.fwd(q2, k2, v2, causal=False)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o_a) and torch.equal(l1, l_a)
+        assert torch.equal(o2, o_b) and torch.equal(l2, l_b)
+        assert torch.equal(do1, do_a) and torch.equal(dl1, dl_a)
