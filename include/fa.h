@@ -141,7 +141,10 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *   M = max_c lse_c;  lse = M + ln sum_c exp(lse_c - M);
  *   o = sum_c exp(lse_c - lse) o_c.
  * (The merge is not on the pages; it is the online-softmax rescale of AV §3
- * applied to whole-chunk summaries.)  Empty chunks contribute nothing.
+ * applied to whole-chunk summaries.)  Empty chunks contribute nothing.  With
+ * num_splits = 1 the single chunk is the answer: the first kernel writes o
+ * and lse itself (the same values the merge would give) and the workspace is
+ * not touched.
  *   q         [B,H,d]          bf16, device
  *   k_cache   [B,H_kv,N_max,d] bf16, device; rows >= seq_lens[b] are never read
  *   v_cache   [B,H_kv,N_max,d] bf16, device; same

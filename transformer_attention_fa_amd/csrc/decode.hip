@@ -83,6 +83,10 @@ struct SplitParams {
     int max_blocks, page_size, num_pages;
     float c;      // scale * log2(e) (times k_scale for an FP8 cache), > 0
     float v_scale;          // FP8 cache: values are v_scale * e4m3 code; 1 otherwise
+    // one chunk per sequence (S == 1): the chunk result is the answer, written
+    // straight to o (bf16) and lse, and the merge kernel is not launched
+    uint16_t* o;
+    float* lse;
 };
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -532,8 +536,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
             oo += a * sh_o[(ww * 16 + hh) * D + ((((d >> 2) ^ hh)) << 2) + (d & 3)];
         }
         const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
-        p.part_o[row * D + d] = ll > 0.f ? oo / ll * p.v_scale : 0.f;
-        if (d == 0) p.part_lse[row] = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
+        const float val = ll > 0.f ? oo / ll * p.v_scale : 0.f;
+        const float lse_c = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
+        if (p.o) {
+            // S == 1 (row indexes (b, h)): the merge of one chunk has weight
+            // exactly 1, so this is the value it would write
+            p.o[row * D + d] = __builtin_bit_cast(uint16_t, __builtin_convertvector((f32x2{val, 0.f}), bf16x2)[0]);
+            if (d == 0 && p.lse) p.lse[row] = lse_c;
+        } else {
+            p.part_o[row * D + d] = val;
+            if (d == 0) p.part_lse[row] = lse_c;
+        }
     }
 }
 
@@ -651,11 +664,13 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     const float sc = KV8 ? a.scale * a.k_scale : a.scale;   // FP8: keys are k_scale * code
     p.c = sc > 0.f ? sc * kLog2e : 1e-30f;
     p.v_scale = KV8 ? a.v_scale : 1.f;
+    p.o = a.num_splits == 1 ? static_cast<uint16_t*>(a.o) : nullptr;
+    p.lse = a.lse;
     const long long gy = (long long)a.H_kv * p.ngrp;
     if (gy > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((decode_split_kernel<D, PAGED, KV8>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.num_splits == 1) return e;
     CombineParams cp{a.part_o, a.part_lse, static_cast<uint16_t*>(a.o), a.lse, a.B * a.H, a.num_splits};
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((cp.rows + 3) / 4), dim3(256), 0, stream, cp);
     return hipGetLastError();

@@ -162,7 +162,7 @@ GQA_DECODE = Decode("gqa_decode_b32_h32_hkv8_d128_len8k_32k_s16", 32, 32, 8, 128
 # bottom-right causal case of "Attention mechanism evolution" KV-cache code).
 SWA_PREFILL = Prefill("swa_prefill_b1_h32_hkv8_n16384_w4096_d128", 1, 32, 8, 16384, 16384, 128, True, "bf16", 6,
                       window=4096)
-SWA_DECODE = Decode("swa_decode_b32_h32_hkv8_d128_len8k_32k_w4096_s2", 32, 32, 8, 128, 8192, 32768, 32768, 2, 5,
+SWA_DECODE = Decode("swa_decode_b32_h32_hkv8_d128_len8k_32k_w4096_s1", 32, 32, 8, 128, 8192, 32768, 32768, 1, 5,
                     window=4096)
 PAGED_DECODE = Decode("paged_decode_b32_h32_hkv8_d128_len8k_32k_p16_s16", 32, 32, 8, 128, 8192, 32768, 32768, 16, 5,
                       page_size=16)
