@@ -688,7 +688,7 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 }  // namespace
 
 #ifndef FA_FWD_GROUP
-#define FA_FWD_GROUP 8
+#define FA_FWD_GROUP 4
 #endif
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream)
