@@ -89,6 +89,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.0f;   // log2 units
+constexpr int kStreamOnce = 2;          // buffer load cache policy: non-temporal
 
 struct Params {
     const uint16_t* q;
@@ -242,12 +243,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         return it;
     };
     // Q block of an item into the Q area (16-byte chunks swizzled like a K
-    // tile); rows past N_q read as 0
+    // tile); rows past N_q read as 0.  Q is read once, so the load is
+    // non-temporal and leaves L2 to the K/V tiles other items re-read.
     auto issue_q = [&](const Item& it, int part) __attribute__((always_inline)) {
         const unsigned bytes = (unsigned)max(0, min(BM, p.N_q - it.q0)) * ROWB;
         const i32x4 rs = make_rsrc(p.q + ((size_t)it.bh * (size_t)p.N_q + (size_t)it.q0) * D, bytes);
         fa_raw_buffer_load_lds(rs, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
-                               ld_voff + part * NTHR * 16, 0, 0, 0);
+                               ld_voff + part * NTHR * 16, 0, 0, kStreamOnce);
     };
 
     Item cur, nxt;
@@ -583,7 +585,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         // wave stages its 32 x D tile in its own 32 rows of the Q area (after
         // taking the next item's Q fragments from there; 16-byte chunks
         // XOR-swizzled by row) and reads it back row-major: every global store
-        // is then 4 (or 8) whole rows, 1 KB contiguous.
+        // is then 4 (or 8) whole rows, 1 KB contiguous, and non-temporal (O is
+        // written once).
         float l_tot;
         {
             const float l_run = l_a + l_b;
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             const int rr = k * RPI + lane / CPR, c = lane % CPR;
             const u32x4 t = *reinterpret_cast<const u32x4*>(qw_lds + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
             if (qw0 + rr < p.N_q)
-                *reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8) = t;
+                __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8));
         }
         if (!has_next) break;
         sb = (j_knext + 1 + sb - nxt.kb_lo) & 1;   // the next item's first K tile sits in slot (j_knext + 1 + sb) % 2
