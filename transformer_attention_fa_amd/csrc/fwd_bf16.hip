@@ -575,18 +575,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         }
         for (; j <= cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{});  // tiles after this wave's rows
 
-        // ---- item switch: the next item's Q block and first K tile landed and
-        //      every wave is done with this item's slots
-        __builtin_amdgcn_s_waitcnt(0x0f70);
-        __syncthreads();
-        // epilogue: O = O_acc / l (bf16), lse = ln2 * (m + log2 l).  A lane
-        // holds 4-element pieces of one row, so storing straight from the
-        // accumulators would write 32 rows x 8 bytes per instruction.  Each
-        // wave stages its 32 x D tile in its own 32 rows of the Q area (after
-        // taking the next item's Q fragments from there; 16-byte chunks
-        // XOR-swizzled by row) and reads it back row-major: every global store
-        // is then 4 (or 8) whole rows, 1 KB contiguous, and non-temporal (O is
-        // written once).
+        // ---- item switch.  Epilogue: O = O_acc / l (bf16), lse = ln2 * (m +
+        //      log2 l).  A lane holds 4-element pieces of one row, so storing
+        //      straight from the accumulators would write 32 rows x 8 bytes per
+        //      instruction.  Each wave stages its 32 x D tile in LDS (16-byte
+        //      chunks XOR-swizzled by row) and reads it back row-major: every
+        //      global store is then 4 (or 8) whole rows, 1 KB contiguous, and
+        //      non-temporal (O is written once).
         float l_tot;
         {
             const float l_run = l_a + l_b;
@@ -596,26 +591,43 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         if (p.lse && half == 0 && qi < p.N_q)
             p.lse[(size_t)cur.bh * (size_t)p.N_q + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
-        if (has_next) read_q();
+        auto stage_store = [&](char* ow) __attribute__((always_inline)) {
 #pragma unroll
-        for (int dm = 0; dm < DBLK; ++dm)
+            for (int dm = 0; dm < DBLK; ++dm)
 #pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-                f32x4 t;
+                for (int gq = 0; gq < 4; ++gq) {
+                    f32x4 t;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
-                const int c = 4 * dm + gq;             // 16-byte chunk of the row (elements 8c .. 8c+7)
-                *reinterpret_cast<bf16x4*>(qw_lds + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
-                    __builtin_convertvector(t, bf16x4);
+                    for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
+                    const int c = 4 * dm + gq;         // 16-byte chunk of the row (elements 8c .. 8c+7)
+                    *reinterpret_cast<bf16x4*>(ow + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
+                        __builtin_convertvector(t, bf16x4);
+                }
+            constexpr int RPI = 64 / CPR;              // rows per wave-wide 16-byte read
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int rr = k * RPI + lane / CPR, c = lane % CPR;
+                const u32x4 t = *reinterpret_cast<const u32x4*>(ow + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
+                if (qw0 + rr < p.N_q)
+                    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8));
             }
-        constexpr int RPI = 64 / CPR;                  // rows per wave-wide 16-byte read
-#pragma unroll
-        for (int k = 0; k < 32 / RPI; ++k) {
-            const int rr = k * RPI + lane / CPR, c = lane % CPR;
-            const u32x4 t = *reinterpret_cast<const u32x4*>(qw_lds + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
-            if (qw0 + rr < p.N_q)
-                __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8));
+        };
+        // The matrix-core-first waves (role 0) end the last period with a
+        // short PV phase, so they stage and store at once, in slots the last
+        // period leaves free, while the other waves finish: the K slot of
+        // tile nkb-1 and the V slot of tile nkb-2 (an item with no key tiles:
+        // both V slots; its next first K tile sits in the other K slot).
+        if (role == 0) {
+            char* free0 = cur.nkb > cur.kb_lo ? lds + ((cur.nkb + 1 + sb) & 1) * TILE : lds + 2 * TILE;
+            char* free1 = cur.nkb > cur.kb_lo ? lds + (2 + ((cur.nkb + sb) & 1)) * TILE : lds + 3 * TILE;
+            stage_store((w < 2 ? free0 : free1) + (w & 1) * 32 * ROWB);
         }
+        // the next item's Q block and first K tile landed, and every wave is
+        // done with this item's slots
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        __syncthreads();
+        if (has_next) read_q();
+        if (role == 1) stage_store(qw_lds);      // after taking the next Q fragments from these rows
         if (!has_next) break;
         sb = (j_knext + 1 + sb - nxt.kb_lo) & 1;   // the next item's first K tile sits in slot (j_knext + 1 + sb) % 2
         cur = nxt;
