@@ -230,8 +230,8 @@ def add_rooflines(nxt):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(each GPU would run its own shard of heads or sequences; see DESIGN.md).", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(each GPU would run its own shard of heads or sequences).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

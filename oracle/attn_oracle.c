@@ -32,7 +32,7 @@
  *  - "Flash Attention: principles and practice" (holysheep.ai), the
  *    conventional three-step computation.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *  - causal alignment when N_q != N_k is bottom-right: query row i sees keys
  *    j <= i + (N_k - N_q); with N_q == N_k this is j <= i;
  *  - a row with no visible key returns o = 0 and lse = -inf;
