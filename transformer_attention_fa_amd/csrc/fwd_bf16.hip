@@ -37,7 +37,10 @@
 //    other slots.  A wave's period has a matrix-core phase (O^T += V^T P^T of
 //    tile j-1, S^T of tile j) and a softmax phase (tile j's P).  Waves 0-3 run
 //    MFMA then softmax, waves 4-7 softmax then MFMA, so on each SIMD one wave's
-//    exponentials overlap the other wave's matrix-core work;
+//    exponentials overlap the other wave's matrix-core work.  Waves 0-3 also
+//    load the two tiles, one load after every other MFMA of their matrix-core
+//    phase (issued by all waves at the barrier, the loads queue up and stall
+//    every wave);
 //  * the matrix-core phase is a two-deep pipeline of steps of four MFMAs: the
 //    next step's LDS fragments are read before this step's MFMAs issue;
 //  * softmax in base 2 (scores scaled by scale*log2(e), v_exp_f32); the
@@ -215,6 +218,23 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             fa_raw_buffer_load_lds(rs, (LDS_AS void*)(dst + (i * NTHR + w * 64) * 16), 16, ld_voff + i * NTHR * 16, 0,
                                    0, 0);
     };
+    // the same tile loaded by waves 0-3 alone: 2*LOADS loads each, load i at
+    // chunk i*NTHR/2 + (w&3)*64 + lane (NTHR/2 chunks are a whole number of
+    // 16-row swizzle periods, so load i is load 0 moved on both sides)
+    constexpr int LOADS0 = 2 * LOADS;
+    int ld_voff0;
+    {
+        const int t = (w & 3) * 64 + lane, r = t / CPR, cp = t % CPR;
+        ld_voff0 = r * ROWB + swz<D>(r, cp) * 16;
+    }
+    auto tile_rsrc = [&](const char* base, int kb) __attribute__((always_inline)) {
+        const int key0 = kb * BN;
+        return make_rsrc(base + (size_t)key0 * ROWB, (unsigned)min(BN, p.N_k - key0) * ROWB);
+    };
+    auto issue0 = [&](const i32x4& rs, char* dst, int i) __attribute__((always_inline)) {
+        fa_raw_buffer_load_lds(rs, (LDS_AS void*)(dst + (i * (NTHR / 2) + (w & 3) * 64) * 16), 16,
+                               ld_voff0 + i * (NTHR / 2) * 16, 0, 0, 0);
+    };
 
     // ---- work items.  Item (query block, head, batch) covers query rows
     //      q0 .. q0+BM-1; the per-wave quantities below are set per item.
@@ -324,6 +344,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     };
     // step st has nmma(st) MFMAs; part k of its fragments is fragment k
     auto nmma = [](int st) constexpr { return st < NPV ? DBLK : 4; };
+    // MFMAs of steps FIRST .. st-1
+    auto mma_index = [](int first, int st) constexpr {
+        int n = 0;
+        for (int i = first; i < st; ++i) n += i < NPV ? DBLK : 4;
+        return n;
+    };
     auto load_part = [&](auto stc, auto kc, Frags& r, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
         constexpr int st = decltype(stc)::value, k = decltype(kc)::value;
         if constexpr (st < NPV) {
@@ -352,7 +378,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     // keep that order (left alone, the compiler groups the reads and sinks
     // them below the MFMAs to reuse their registers, and the read latency or
     // issue time lands on every step).
-    auto run_steps = [&](auto firstc, auto lastc, const char* kt_lds, const char* vt_lds) __attribute__((always_inline)) {
+    auto run_steps = [&](auto firstc, auto lastc, const char* kt_lds, const char* vt_lds, auto&& after_mma) __attribute__((always_inline)) {
         constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value;
         Frags cur;
         static_for<0, nmma(FIRST)>([&](auto kc) __attribute__((always_inline)) {
@@ -368,6 +394,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 constexpr int k = decltype(kc)::value;
                 if constexpr (k < NM) {
                     mma_part(stc, kc, cur);
+                    after_mma(std::integral_constant<int, mma_index(FIRST, st) + k>{});
                     __builtin_amdgcn_sched_barrier(0);
                 }
                 if constexpr (k < NL) {
@@ -468,17 +495,42 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     // slots, and saying so keeps the compiler from waiting for the loads
     // before the first read (their order across periods comes from the
     // explicit wait and the barrier).
-    auto period = [&](int j, auto firstc, auto lastc, auto smc, char* __restrict__ kdst, char* __restrict__ vdst,
+    auto period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, char* __restrict__ kdst, char* __restrict__ vdst,
                       const char* __restrict__ kt, const char* __restrict__ vt) __attribute__((always_inline)) {
         constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value, SM = decltype(smc)::value;
+        constexpr int ROLE = decltype(rolec)::value;     // 0, 1, or 2 = either (no matrix-core phase)
         // this wave's loads of the previous period landed (the item's first
         // period follows the item switch, which waited already)
         if (j != cur.kb_lo) __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
-        if (j + 1 < cur.nkb) issue(kbase, j + 1, kdst);
-        else if (has_next && j == j_knext)
-            issue(reinterpret_cast<const char*>(p.k + (size_t)nxt.bg * (size_t)p.N_k * D), nxt.kb_lo, kdst);
-        if (j < cur.nkb) issue(vbase, j, vdst);
+        // K tile j+1 (or the next item's first) and V tile j.  Waves 0-3 load
+        // them, one load after every other MFMA of their matrix-core phase:
+        // those waves wait for the matrix core there anyway, while eight waves
+        // issuing 32 loads at the barrier stall on the shared issue queue.
+        // Without a matrix-core phase in this period they load at once.
+        const bool ldk = j + 1 < cur.nkb || (has_next && j == j_knext);
+        const bool ldv = j < cur.nkb;
+        const i32x4 rk = j + 1 < cur.nkb ? tile_rsrc(kbase, j + 1)
+                                         : tile_rsrc(reinterpret_cast<const char*>(p.k + (size_t)nxt.bg * (size_t)p.N_k * D), nxt.kb_lo);
+        const i32x4 rv = tile_rsrc(vbase, j);
+        auto spread = [&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i % 2 == 0 && i / 2 < LOADS0) {
+                if (ldk) issue0(rk, kdst, i / 2);
+            } else if constexpr (i % 2 == 0 && i / 2 < 2 * LOADS0) {
+                if (ldv) issue0(rv, vdst, i / 2 - LOADS0);
+            }
+        };
+        constexpr bool has_mma = FIRST < LAST;
+        static_assert(has_mma == (ROLE != 2), "a role with a matrix-core phase");
+        static_assert(!has_mma || 2 * (2 * LOADS0) <= mma_index(FIRST, LAST), "every load fits in the phase");
+        if (!has_mma && role == 0) {
+#pragma unroll
+            for (int i = 0; i < LOADS0; ++i) {
+                if (ldk) issue0(rk, kdst, i);
+                if (ldv) issue0(rv, vdst, i);
+            }
+        }
         if (has_next) {
             const int part_lo = min(QPARTS, j - cur.kb_lo);
             const int part_hi = j == cur.nkb ? QPARTS : min(QPARTS, j - cur.kb_lo + 1);
@@ -488,7 +540,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         if constexpr (SM == 1) softmax_phase(j - 1);
         if constexpr (FIRST < LAST) {
             __builtin_amdgcn_s_setprio(1);           // matrix-core phase first when both waves are ready
-            run_steps(firstc, lastc, kt, vt);
+            if constexpr (ROLE == 0) run_steps(firstc, lastc, kt, vt, spread);
+            else run_steps(firstc, lastc, kt, vt, [](auto) {});
             __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -496,9 +549,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     };
     // slots of period j: K tile j+1 and V tile j load, K tile j and V tile j-1
     // are read
-    auto run_period = [&](int j, auto firstc, auto lastc, auto smc) __attribute__((always_inline)) {
+    auto run_period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec) __attribute__((always_inline)) {
         const int b = (j + sb) & 1;
-        period(j, firstc, lastc, smc, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE, lds + b * TILE,
+        period(j, firstc, lastc, smc, rolec, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE, lds + b * TILE,
                lds + (2 + (b ^ 1)) * TILE);
     };
     using C0 = std::integral_constant<int, 0>;
@@ -560,20 +613,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         l_b = 0.f;
 
         int j = cur.kb_lo;
-        for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{});    // tiles before this wave's window
+        for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{}, C2{});    // tiles before this wave's window
         if (nkb_w > a_w) {
             if (role == 0) {
-                run_period(j, CNPV{}, CNSTEP{}, C2{});
-                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{});
-                run_period(j, C0{}, CNPV{}, C0{});            // j == nkb_w: PV of the last tile
+                run_period(j, CNPV{}, CNSTEP{}, C2{}, C0{});
+                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{});
+                run_period(j, C0{}, CNPV{}, C0{}, C0{});            // j == nkb_w: PV of the last tile
             } else {
-                run_period(j, CNPV{}, CNSTEP{}, C0{});
-                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{});
-                run_period(j, C0{}, CNPV{}, C1{});
+                run_period(j, CNPV{}, CNSTEP{}, C0{}, C1{});
+                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{});
+                run_period(j, C0{}, CNPV{}, C1{}, C1{});
             }
             ++j;
         }
-        for (; j <= cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{});  // tiles after this wave's rows
+        for (; j <= cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{}, C2{});  // tiles after this wave's rows
 
         // ---- item switch.  Epilogue: O = O_acc / l (bf16), lse = ln2 * (m +
         //      log2 l).  A lane holds 4-element pieces of one row, so storing
