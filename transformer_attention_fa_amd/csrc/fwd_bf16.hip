@@ -54,11 +54,17 @@
 //    its workgroups take the list in rounds that alternate direction (a long
 //    causal block in one round pairs with a short one in the next);
 //  * item switch without a cold start: while an item runs, the next item's Q
-//    block streams into its own LDS area (one slice per period) and its first
-//    K tile into the K slot the last period leaves free; at the switch each
-//    wave takes its Q fragments from that area, then stages its finished
-//    32 x d output tile in the same rows and stores it as whole rows, and the
-//    next item's first period starts without waiting for those stores.
+//    block streams into its own LDS area (one slice per period, all of it
+//    before the last period) and its first K tile into the K slot the last
+//    period leaves free.  After its last tile each wave takes its next Q
+//    fragments from that area, stages its finished 32 x d output tile in the
+//    same rows, and holds it in registers across the switch barrier; the
+//    whole-row stores issue after the barrier, so its wait for the next
+//    item's loads does not wait for them, and the next item's first period
+//    starts without waiting either;
+//  * waves 0-3 take the block's later rows: on the causal diagonal those run
+//    longest, and a matrix-core-first wave ends with a lone PV phase, so the
+//    item's last period is short.
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -198,6 +204,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     const int l32 = lane & 31;
     const int half = lane >> 5;
     const int role = w >> 2;                 // waves w and w+4 share a SIMD
+    // Row groups: waves 0-3 take rows 128-255 of the block, waves 4-7 rows
+    // 0-127.  On the causal diagonal the later rows run longest, and a
+    // matrix-core-first wave ends its last tile with a PV phase alone (its
+    // softmax of that tile ran in the period before), so the item's last
+    // period is short.
+    const int wr = w ^ 4;
     const int off = p.N_k - p.N_q;           // causal diagonal offset
 
     // ---- tile loads: chunk position -> (row, global chunk).  A workgroup-wide
@@ -283,7 +295,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     auto set_wave = [&]() __attribute__((always_inline)) {
         kbase = reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D);
         vbase = reinterpret_cast<const char*>(p.v + (size_t)cur.bg * (size_t)p.N_k * D);
-        qw0 = cur.q0 + w * 32;               // first row of this wave
+        qw0 = cur.q0 + wr * 32;              // first row of this wave
         qi = qw0 + l32;                      // this lane's query row
         last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
         // tiles this wave computes: a_w .. nkb_w-1.  Later tiles lie after its
@@ -474,6 +486,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         __builtin_amdgcn_sched_barrier(0);
     };
 
+    // Q fragments of an item from the Q area (this wave's 32 rows)
+    char* const qw_lds = qarea + wr * 32 * ROWB;
+    auto read_q = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qw_lds + k_off[ks]);
+    };
+
     // ---- periods j = kb_lo .. nkb of an item.  In period j every wave reads
     //      K tile j and V tile j-1 only, while K tile j+1 and V tile j load
     //      into the other slots.  The two waves that share a SIMD run the two
@@ -495,8 +514,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     // slots, and saying so keeps the compiler from waiting for the loads
     // before the first read (their order across periods comes from the
     // explicit wait and the barrier).
-    auto period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, char* __restrict__ kdst, char* __restrict__ vdst,
-                      const char* __restrict__ kt, const char* __restrict__ vt) __attribute__((always_inline)) {
+    auto period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, char* __restrict__ kdst,
+                      char* __restrict__ vdst, const char* __restrict__ kt, const char* __restrict__ vt)
+                      __attribute__((always_inline)) {
         constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value, SM = decltype(smc)::value;
         constexpr int ROLE = decltype(rolec)::value;     // 0, 1, or 2 = either (no matrix-core phase)
         // this wave's loads of the previous period landed (the item's first
@@ -531,9 +551,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 if (ldv) issue0(rv, vdst, i);
             }
         }
+        // The next item's Q block: one part per period, the rest in period
+        // nkb-1, so that it has landed when the last period starts (an item
+        // without key tiles has one period, which loads it all).
         if (has_next) {
+            const int last_q = cur.nkb > cur.kb_lo ? cur.nkb - 1 : cur.nkb;
             const int part_lo = min(QPARTS, j - cur.kb_lo);
-            const int part_hi = j == cur.nkb ? QPARTS : min(QPARTS, j - cur.kb_lo + 1);
+            const int part_hi = j == last_q ? QPARTS : j < last_q ? min(QPARTS, j - cur.kb_lo + 1) : part_lo;
             for (int part = part_lo; part < part_hi; ++part) issue_q(nxt, part);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -560,12 +584,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     using CNPV = std::integral_constant<int, NPV>;
     using CNSTEP = std::integral_constant<int, NSTEP>;
 
-    // Q fragments of the current item from the Q area (this wave's 32 rows)
-    char* const qw_lds = qarea + w * 32 * ROWB;
-    auto read_q = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const bf16x8*>(qw_lds + k_off[ks]);
-    };
 
     // ---- the workgroup's items: round r of a persistent grid of p.grid
     //      workgroups.  The list splits per XCD when the head count divides by
@@ -644,7 +662,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         if (p.lse && half == 0 && qi < p.N_q)
             p.lse[(size_t)cur.bh * (size_t)p.N_q + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
-        auto stage_store = [&](char* ow) __attribute__((always_inline)) {
+        constexpr int RPI = 64 / CPR;                  // rows per wave-wide 16-byte read
+        u32x4 pend[32 / RPI];                          // this wave's output rows, row-major
+        auto stage = [&](char* ow) __attribute__((always_inline)) {
 #pragma unroll
             for (int dm = 0; dm < DBLK; ++dm)
 #pragma unroll
@@ -656,31 +676,39 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                     *reinterpret_cast<bf16x4*>(ow + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
                         __builtin_convertvector(t, bf16x4);
                 }
-            constexpr int RPI = 64 / CPR;              // rows per wave-wide 16-byte read
 #pragma unroll
             for (int k = 0; k < 32 / RPI; ++k) {
                 const int rr = k * RPI + lane / CPR, c = lane % CPR;
-                const u32x4 t = *reinterpret_cast<const u32x4*>(ow + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
-                if (qw0 + rr < p.N_q)
-                    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8));
+                pend[k] = *reinterpret_cast<const u32x4*>(ow + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
             }
         };
-        // The matrix-core-first waves (role 0) end the last period with a
-        // short PV phase, so they stage and store at once, in slots the last
-        // period leaves free, while the other waves finish: the K slot of
-        // tile nkb-1 and the V slot of tile nkb-2 (an item with no key tiles:
-        // both V slots; its next first K tile sits in the other K slot).
-        if (role == 0) {
-            char* free0 = cur.nkb > cur.kb_lo ? lds + ((cur.nkb + 1 + sb) & 1) * TILE : lds + 2 * TILE;
-            char* free1 = cur.nkb > cur.kb_lo ? lds + (2 + ((cur.nkb + sb) & 1)) * TILE : lds + 3 * TILE;
-            stage_store((w < 2 ? free0 : free1) + (w & 1) * 32 * ROWB);
+        auto store_pend = [&]() __attribute__((always_inline)) {
+#pragma unroll
+            for (int k = 0; k < 32 / RPI; ++k) {
+                const int rr = k * RPI + lane / CPR, c = lane % CPR;
+                if (qw0 + rr < p.N_q)
+                    __builtin_nontemporal_store(pend[k], reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8));
+            }
+        };
+        // The next item's Q block landed before the last period (see the
+        // period's loads), so every wave takes its next Q fragments now,
+        // stages its output in those same rows of the Q area, and holds the
+        // output in registers across the switch barrier: the stores issue
+        // after it, so the barrier's wait for the next item's loads does not
+        // also wait for them.  An item without key tiles loads the next Q
+        // block in its only period: it does all of that after the barrier.
+        const bool late_q = has_next && cur.nkb == cur.kb_lo;
+        if (!late_q) {
+            if (has_next) read_q();
+            stage(qw_lds);
         }
-        // the next item's Q block and first K tile landed, and every wave is
-        // done with this item's slots
         __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
-        if (has_next) read_q();
-        if (role == 1) stage_store(qw_lds);      // after taking the next Q fragments from these rows
+        if (late_q) {
+            read_q();
+            stage(qw_lds);
+        }
+        store_pend();
         if (!has_next) break;
         sb = (j_knext + 1 + sb - nxt.kb_lo) & 1;   // the next item's first K tile sits in slot (j_knext + 1 + sb) % 2
         cur = nxt;
