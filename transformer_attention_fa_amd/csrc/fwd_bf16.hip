@@ -288,6 +288,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     bool has_next;
     int sb;                  // slot parity: tile t of the current item lives in slot (t + sb) % 2
     int j_knext;             // period that loads the next item's first K tile
+    int qpp;                 // parts of the next item's Q block loaded per period
     const char* kbase;
     const char* vbase;
     int qw0, qi, last_vis, first_vis, nkb_w, a_w;
@@ -551,13 +552,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 if (ldv) issue0(rv, vdst, i);
             }
         }
-        // The next item's Q block: one part per period, the rest in period
-        // nkb-1, so that it has landed when the last period starts (an item
-        // without key tiles has one period, which loads it all).
+        // The next item's Q block: qpp parts per period over periods kb_lo ..
+        // nkb-1, so that it has landed when the last period starts; qpp is the
+        // smallest power of two that fits them in (1 for items of QPARTS
+        // tiles or more: a short item does not load it all in one burst).  An
+        // item without key tiles has one period, which loads it all.
         if (has_next) {
-            const int last_q = cur.nkb > cur.kb_lo ? cur.nkb - 1 : cur.nkb;
-            const int part_lo = min(QPARTS, j - cur.kb_lo);
-            const int part_hi = j == last_q ? QPARTS : j < last_q ? min(QPARTS, j - cur.kb_lo + 1) : part_lo;
+            const int part_lo = min(QPARTS, (j - cur.kb_lo) * qpp);
+            const int part_hi = min(QPARTS, (j - cur.kb_lo + 1) * qpp);
             for (int part = part_lo; part < part_hi; ++part) issue_q(nxt, part);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -622,6 +624,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         has_next = PERSIST && nid >= 0;
         nxt = has_next ? item_at(nid) : cur;
         j_knext = max(cur.kb_lo, cur.nkb - 1);
+        qpp = 1;
+        while (qpp < QPARTS && qpp * (cur.nkb - cur.kb_lo) < QPARTS) qpp *= 2;
         set_wave();
 #pragma unroll
         for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
