@@ -54,9 +54,10 @@
 //    its workgroups take the list in rounds that alternate direction (a long
 //    causal block in one round pairs with a short one in the next);
 //  * item switch without a cold start: while an item runs, the next item's Q
-//    block streams into its own LDS area (one slice per period, all of it
-//    before the last period) and its first K tile into the K slot the last
-//    period leaves free.  After its last tile each wave takes its next Q
+//    block streams into its own LDS area (spread over the item's periods,
+//    one slice per period when the item is long enough, all of it before the
+//    last period) and its first K tile into the K slot the last period
+//    leaves free.  After its last tile each wave takes its next Q
 //    fragments from that area, stages its finished 32 x d output tile in the
 //    same rows, and holds it in registers across the switch barrier; the
 //    whole-row stores issue after the barrier, so its wait for the next
