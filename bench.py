@@ -17,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -45,10 +46,15 @@ def parse():
 
 
 def kernel_source_hash(files):
+    """Hash of the kernel sources' code: comments and whitespace are dropped,
+    so that editing a comment does not disown the committed counter figures."""
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, "transformer_attention_fa_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "transformer_attention_fa_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
