@@ -423,22 +423,53 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     auto softmax_phase = [&](int j) __attribute__((always_inline)) {
         const int key0 = j * BN;
         const bool need_mask = (key0 + BN > p.N_k) || (CAUSAL && key0 + BN - 1 > qw0 + off);
+        // Element masks.  Lane (l32, half) holds keys kt*32 + 8*(r/4) + r%4 +
+        // 4*half of sub-tile kt.  A 32-key sub-tile that every row of the wave
+        // sees whole, or that none of them sees, is settled per wave.  Inside
+        // a straddling one the lane builds a 32-bit word with bit k set when
+        // key k of the sub-tile is visible, and each score tests its own bit,
+        // so the tests are independent.  Written as compares against a key
+        // limit, the compiler sees that the conditions are monotone and
+        // chains them through the scalar unit, one dependent step per score.
+        auto apply_mask = [&](int kt, unsigned vis) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (!((vis >> (8 * (r >> 2) + (r & 3))) & 1u)) s[kt][r] = kNegInf;
+        };
+        // bits 0 .. n-1 set (n clamped to 0 .. 32)
+        auto low_bits = [](int n) __attribute__((always_inline)) {
+            return n >= 32 ? 0xffffffffu : n <= 0 ? 0u : (1u << n) - 1u;
+        };
         if (need_mask) {
             const int lim = last_vis - key0 - 4 * half;
+            const int vis_lo = (CAUSAL ? min(qw0 + off, p.N_k - 1) : p.N_k - 1) - key0;   // over the wave's rows
+            const int vis_hi = (CAUSAL ? min(qw0 + 31 + off, p.N_k - 1) : p.N_k - 1) - key0;
 #pragma unroll
-            for (int kt = 0; kt < NT; ++kt)
+            for (int kt = 0; kt < NT; ++kt) {
+                if (kt * 32 + 31 <= vis_lo) continue;
+                if (kt * 32 > vis_hi) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kt * 32 + 8 * (r >> 2) + (r & 3) > lim) s[kt][r] = kNegInf;
+                    for (int r = 0; r < 16; ++r) s[kt][r] = kNegInf;
+                } else {
+                    apply_mask(kt, low_bits(lim - kt * 32 + 1));      // keys <= lim
+                }
+            }
         }
         // keys before the window of some row of this wave
         if (windowed && key0 < qw0 + 31 + off - p.window + 1) {
             const int lo = first_vis - key0 - 4 * half;
+            const int win_lo = qw0 + off - p.window + 1 - key0;      // over the wave's rows
+            const int win_hi = qw0 + 31 + off - p.window + 1 - key0;
 #pragma unroll
-            for (int kt = 0; kt < NT; ++kt)
+            for (int kt = 0; kt < NT; ++kt) {
+                if (kt * 32 >= win_hi) continue;
+                if (kt * 32 + 31 < win_lo) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    if (kt * 32 + 8 * (r >> 2) + (r & 3) < lo) s[kt][r] = kNegInf;
+                    for (int r = 0; r < 16; ++r) s[kt][r] = kNegInf;
+                } else {
+                    apply_mask(kt, ~low_bits(lo - kt * 32));           // keys >= lo
+                }
+            }
         }
         // row max of the tile; the running max is raised only when it grows by
         // more than the slack (then O and l are rescaled)
