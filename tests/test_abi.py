@@ -81,6 +81,9 @@ FWD_CASES = [
     ("v_misaligned", dict(v=P + 2), INVALID),
     ("lse_misaligned", dict(lse=P + 2), INVALID),
     ("too_large", dict(B=1 << 20, H=1 << 10, N_q=1 << 12, N_k=1 << 12), UNSUPPORTED),
+    # B*H is exactly at the 2^40 cap and N_q is huge: the size check must not
+    # form the 2^70 product (signed overflow) on its way to rejecting it
+    ("too_large_no_overflow", dict(B=1 << 20, H=1 << 20, H_kv=1 << 20, N_q=1 << 30, N_k=1), UNSUPPORTED),
 ]
 
 

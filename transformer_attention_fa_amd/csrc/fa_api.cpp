@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <initializer_list>
 
 namespace {
 
@@ -28,11 +29,18 @@ fa_status_t fail(fa_status_t s, const char* fmt, ...)
 
 bool aligned(const void* p, std::uintptr_t n) { return (reinterpret_cast<std::uintptr_t>(p) % n) == 0; }
 
-// Element counts stay far below 2^62; the kernels index with 64-bit offsets.
+// Element counts are capped at 2^40 (the kernels index with 64-bit offsets).
+// Each partial product is checked before it is formed, so no product of
+// positive sizes can overflow.
 bool too_large(long long a, long long b, long long c, long long d)
 {
     const long long lim = 1LL << 40;
-    return a * b > lim || a * b * c > lim || a * b * c * d > lim;
+    long long prod = a;
+    for (long long x : {b, c, d}) {
+        if (x > 0 && prod > lim / x) return true;
+        prod *= x;
+    }
+    return prod > lim;
 }
 
 fa_status_t check_common(const void* q, const void* k, const void* v, const void* o, const float* lse,
