@@ -488,8 +488,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
             l_a *= alpha;
             l_b *= alpha;
+            // O is still the zero it started at until some row of the wave
+            // has seen a key (the item's first tile always lands here)
+            if (__builtin_amdgcn_ballot_w64(m_run != kNegInf)) {
 #pragma unroll
-            for (int dm = 0; dm < DBLK; ++dm) oacc[dm] *= alpha;
+                for (int dm = 0; dm < DBLK; ++dm) oacc[dm] *= alpha;
+            }
             m_run = m_new;
             nbase = (m_new == kNegInf) ? 0.f : -m_new;
         }
