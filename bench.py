@@ -105,7 +105,21 @@ def cpu_baseline(spec, n_batches):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": (f"the whole {spec.name} workload" if n_batches == spec.B else
                        f"{n_batches} of {spec.B} sequences ({n_batches * spec.H} heads) of {spec.name}")
-                      + f", fp64, {dt:.2f} s wall"}
+                      + f", fp64, {dt:.2f} s wall",
+            "cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
+
+
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo when there is one."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def time_launches(fn, steps, warmup):
@@ -143,7 +157,8 @@ def measure_next(dev_bf16, steps, warmup, decode_state=None):
         tf = flops / (avg * 1e-3) / 1e12
         out[spec.name] = {"entry": "fa_fwd_window" if win else "fa_fwd", "value": tf, "unit": "TFLOP/s",
                           "frac_mfma_peak": tf / roofline.PEAK_BF16_TFLOPS, "ms_avg": avg, "ms_median": med,
-                          "ms_min": mn, "flop_per_launch": flops, "window": spec.window,
+                          "ms_min": mn, "flop_per_launch": flops, "exp_per_launch": flops / (4 * spec.d),
+                          "window": spec.window,
                           "shape": {"B": spec.B, "H": spec.H, "H_kv": spec.H_kv, "N_q": spec.N_q, "N_k": spec.N_k,
                                     "d": spec.d, "causal": spec.causal}}
         del q, k, v, o, lse
@@ -329,6 +344,9 @@ def main():
                            "kernel": "fwd_bf16_kernel", "launch_ms_avg": t_avg,
                            "launch_ms_median": float(np.median(t_pf)), "launch_ms_min": float(np.min(t_pf)),
                            "flop_per_launch": flops,
+                           # exponentials per launch (one per visible score): the VALU /
+                           # transcendental budget beside the MFMA work
+                           "exp_per_launch": flops / (4 * pspec.d),
                            "counters": counters_for(f"fwd_bf16:{pspec.name}", ["fwd_bf16.hip"])}
         config["workload"] = pspec.name
         config["prefill"] = {"B": pspec.B, "H": pspec.H, "H_kv": pspec.H_kv, "N_q": pspec.N_q, "N_k": pspec.N_k,
