@@ -299,6 +299,48 @@ def test_fwd_persistent_rounds(case, cap, _grid_cap):
     assert torch.equal(o, o2) and torch.equal(lse, lse2)
 
 
+# ------------------------------------------------------------------ random sweep
+def _random_cases(n, seed=2024):
+    """Seeded shapes that mix what the fixed cases test one at a time: lengths on
+    and around tile (64 keys) and wave (32 rows) boundaries, N_q != N_k, head
+    sharing, both head sizes, causal or not, sliding windows, and caps on the
+    persistent grid (several items per workgroup)."""
+    rng = np.random.default_rng(seed)
+    edges = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 511, 513]
+    cases = []
+    for _ in range(n):
+        n_q = int(rng.choice(edges)) if rng.random() < 0.6 else int(rng.integers(1, 600))
+        n_k = int(rng.choice(edges)) if rng.random() < 0.6 else int(rng.integers(1, 600))
+        h_kv = int(rng.choice([1, 2, 4]))
+        rep = int(rng.choice([1, 2, 3, 4]))
+        b = int(rng.integers(1, 4))
+        d = int(rng.choice([64, 128]))
+        causal = bool(rng.random() < 0.65)
+        window = int(rng.integers(1, n_k + 64)) if causal and rng.random() < 0.4 else None
+        cap = int(rng.choice([0, 0, 1, 3, 8]))
+        cases.append((b, h_kv * rep, h_kv, n_q, n_k, d, causal, window, cap))
+    return cases
+
+
+RANDOM_CASES = _random_cases(24)
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=lambda c: "x".join(str(x) for x in c))
+def test_fwd_random_shapes(case, _grid_cap):
+    import torch
+    B, H, H_kv, N_q, N_k, d, causal, window, cap = case
+    spec = _spec(B, H, H_kv, N_q, N_k, d, causal, seed=41)
+    say(f"fa_fwd random {spec.name} window={window} cap={cap}")
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    api.fwd_set_max_workgroups(cap)
+    o, lse = api.fwd(q, k, v, causal=causal, scale=spec.scale, window=window)
+    torch.cuda.synchronize()
+    api.fwd_set_max_workgroups(0)
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, causal, window=window)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
 # ------------------------------------------------------------------ sliding window
 WINDOW_BF16 = [
     # B, H, H_kv, N_q, N_k, d, window
