@@ -402,6 +402,48 @@ def test_decode_window(window, num_splits):
             label=f"window {window} S={num_splits}")
 
 
+def _random_decode_cases(n, seed=2025):
+    """Seeded decode shapes: one or several head groups per KV head (up to 16
+    query heads per group), both head sizes, cache lengths from 1 to N_max
+    (padding rows poisoned), split counts that do and do not divide them, and
+    sliding windows."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        b = int(rng.integers(1, 9))
+        h_kv = int(rng.choice([1, 2, 4, 8]))
+        rep = int(rng.choice([1, 2, 3, 4, 8, 16, 20]))
+        d = int(rng.choice([64, 128]))
+        n_max = int(rng.choice([1, 17, 300, 2000]))
+        lens = rng.integers(1, n_max + 1, size=b)
+        lens[rng.random(b) < 0.25] = n_max
+        lens[rng.random(b) < 0.15] = 1
+        splits = int(rng.choice([1, 3, 16, 37]))
+        window = int(rng.integers(1, n_max + 20)) if rng.random() < 0.35 else None
+        cases.append((b, h_kv * rep, h_kv, d, n_max, tuple(int(x) for x in lens), splits, window))
+    return cases
+
+
+RANDOM_DECODE_CASES = _random_decode_cases(16)
+
+
+@pytest.mark.parametrize("case", RANDOM_DECODE_CASES,
+                         ids=lambda c: f"B{c[0]}_H{c[1]}_Hkv{c[2]}_d{c[3]}_N{c[4]}_S{c[6]}_w{c[7]}")
+def test_decode_random_shapes(case):
+    import torch
+    B, H, H_kv, d, N_max, lens, S, window = case
+    spec = inputs.Decode(f"decode_B{B}_H{H}_Hkv{H_kv}_d{d}_N{N_max}", B, H, H_kv, d, 1, N_max, N_max, S, 43)
+    lens = np.array(lens, np.int32)
+    say(f"fa_decode random {spec.name} lens={lens.tolist()} splits={S} window={window}")
+    data = inputs.decode_inputs(spec, seq_lens=lens)          # rows past each length hold NaN
+    q = bf16_to_device(data.q)
+    kc, vc = bf16_to_device(data.k_cache), bf16_to_device(data.v_cache)
+    o, lse = api.decode(q, kc, vc, torch.from_numpy(lens).cuda(), num_splits=S, scale=spec.scale, window=window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, lens, spec.scale, window=window)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
 @pytest.mark.parametrize("spec", [inputs.SWA_PREFILL, inputs.CHUNKED_PREFILL], ids=lambda s: s.name)
 def test_fwd_next_workloads_sampled(spec):
     import torch
