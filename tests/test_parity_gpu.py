@@ -575,6 +575,56 @@ def test_decode_fp8(H, H_kv, d, num_splits):
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
 
 
+def _random_cache_cases(n, seed=2026):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        b = int(rng.integers(1, 7))
+        h_kv = int(rng.choice([1, 2, 4]))
+        rep = int(rng.choice([1, 3, 4, 16, 18]))
+        d = int(rng.choice([64, 128]))
+        n_max = int(rng.choice([16, 100, 1500]))
+        lens = rng.integers(1, n_max + 1, size=b)
+        lens[rng.random(b) < 0.25] = n_max
+        splits = int(rng.choice([1, 5, 16]))
+        page = int(rng.choice([16, 32, 48, 128]))
+        cases.append((b, h_kv * rep, h_kv, d, n_max, tuple(int(x) for x in lens), splits, page))
+    return cases
+
+
+RANDOM_CACHE_CASES = _random_cache_cases(10)
+
+
+@pytest.mark.parametrize("case", RANDOM_CACHE_CASES,
+                         ids=lambda c: f"B{c[0]}_H{c[1]}_Hkv{c[2]}_d{c[3]}_N{c[4]}_S{c[6]}_p{c[7]}")
+def test_decode_paged_and_fp8_random_shapes(case):
+    """Seeded shapes for the paged cache (page sizes that are multiples of 16,
+    pages in shuffled order) and the FP8 cache (scales that are powers of two and
+    not), each against its oracle."""
+    import torch
+    B, H, H_kv, d, N_max, lens, S, page = case
+    lens = np.array(lens, np.int32)
+    spec = inputs.Decode(f"rnd_B{B}_H{H}_Hkv{H_kv}_d{d}_N{N_max}", B, H, H_kv, d, 1, N_max, N_max, S, 47)
+    data = inputs.decode_inputs(spec, seq_lens=lens)
+    kp, vp, table = _paged(data, page, 53)
+    say(f"fa_decode_paged random {spec.name} lens={lens.tolist()} S={S} page={page}")
+    o, lse = api.decode_paged(bf16_to_device(data.q), bf16_to_device(kp), bf16_to_device(vp),
+                              torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(), num_splits=S,
+                              scale=spec.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode_paged(data.q, kp, vp, np.maximum(table, 0), lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"paged {spec.name}")
+
+    k_scale, v_scale = (2.0 ** -6, 0.0173) if B % 2 else (0.011, 2.0 ** -5)
+    fspec = inputs.Decode(f"rnd8_B{B}_H{H}_Hkv{H_kv}_d{d}_N{N_max}", B, H, H_kv, d, 1, N_max, N_max, S, 59,
+                          dtype="e4m3", k_scale=k_scale, v_scale=v_scale)
+    fdata = inputs.decode_inputs_fp8(fspec, seq_lens=lens)
+    say(f"fa_decode_fp8 random {fspec.name} k_scale={k_scale} v_scale={v_scale}")
+    o, lse = _fp8_run(fdata, S, k_scale, v_scale)
+    o_ref, lse_ref = oracle.decode_fp8(fdata.q, fdata.k_cache, fdata.v_cache, k_scale, v_scale, lens, fspec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"fp8 {fspec.name}")
+
+
 def test_decode_fp8_every_code():
     """Random codes over the whole finite range (subnormals, zeros of both signs,
     +-448) with scales that are not powers of two."""
