@@ -308,3 +308,47 @@ def decode_inputs_fp8(spec: Decode, seq_lens=None) -> DecodeData:
             c[b, :, int(lens[b]):, :] = E4M3_NAN
         caches.append(c)
     return DecodeData(spec, q, caches[0], caches[1], lens)
+
+
+# ---------------------------------------------------------------- tensors past 4 GiB
+# A tensor of billions of elements is too large to draw on the host and to hand
+# to the fp64 oracle whole.  Its rows repeat a short seeded table instead: row r
+# of a block with shift s is table row (r + s) % period.  The period 8191 is
+# 2^13 - 1, so 2^k = 2^(k mod 13) (mod 8191): moving 2^k rows (k >= 13) never
+# lands on the same table row.  With 256-byte rows (d = 128, bf16) an address
+# that wrapped at 2^31 or 2^32 bytes (2^23 or 2^24 rows) would read a row other
+# than the right one, so the check of a sampled row catches it.
+LARGE_PERIOD = 8191
+
+
+def periodic_table(seed: int, tag: int, d: int, period: int = LARGE_PERIOD) -> np.ndarray:
+    """bf16 bits [period, d]: the row table, N(0,1) rounded to bf16."""
+    rng = np.random.default_rng([seed, tag, period])
+    return f32_to_bf16_bits(rng.standard_normal((period, d), dtype=np.float32))
+
+
+def periodic_rows(start: int, stop: int, shift: int, period: int = LARGE_PERIOD) -> np.ndarray:
+    """Table row of each of the rows start .. stop-1 of a block with the given shift."""
+    return (np.arange(start, stop, dtype=np.int64) + int(shift)) % period
+
+
+def scattered_page_table(seq_lens, page_size: int, num_pages: int, seed: int) -> np.ndarray:
+    """int32 [B, max_blocks] block table over a pool of num_pages pages, its
+    distinct pages drawn (seeded) from the pool's first 64 pages, the 128 around
+    page 2^16 and its last 512, so that a large pool is read near its start,
+    around 2^16 pages and at its end.  Entries past a sequence's last block are -1."""
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    blocks = [(int(n) + page_size - 1) // page_size for n in lens]
+    mid = 1 << 16
+    cand = np.unique(np.concatenate([np.arange(0, 64), np.arange(mid - 64, mid + 64),
+                                     np.arange(num_pages - 512, num_pages)]))
+    cand = cand[(cand >= 0) & (cand < num_pages)]
+    if sum(blocks) > cand.size:
+        raise ValueError("pool too small for the sequences")
+    pick = np.random.default_rng([seed, 9]).permutation(cand)[:sum(blocks)]
+    table = np.full((len(lens), max(blocks)), -1, dtype=np.int32)
+    at = 0
+    for b, n in enumerate(blocks):
+        table[b, :n] = pick[at:at + n]
+        at += n
+    return table
