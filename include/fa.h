@@ -52,7 +52,13 @@
  *    (FA_ERR_INVALID_ARGUMENT / FA_ERR_UNSUPPORTED) and nothing is written.
  *    A failed launch returns FA_ERR_HIP.  fa_last_error() gives a message for
  *    the calling thread's last failure.  Nothing throws across the ABI.
- *  - Thread safety: no global mutable state besides the per-thread message.
+ *  - Sizes: each tensor may hold up to 2^40 elements (larger problems return
+ *    FA_ERR_UNSUPPORTED); the kernels address memory with 64-bit offsets, so
+ *    a tensor may span more than 4 GiB.
+ *  - Thread safety: calls may come from any thread.  The process-wide state is
+ *    the per-thread message, the workgroup cap of fa_fwd_set_max_workgroups
+ *    (an atomic) and a per-device cache of how many prefill workgroups fit on
+ *    the device (filled once, the same value by every thread).
  */
 #ifndef FA_H
 #define FA_H
