@@ -341,6 +341,33 @@ def test_fwd_random_shapes(case, _grid_cap):
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
 
 
+def _random_f32_cases(n, seed=2027):
+    """Seeded fp32 shapes: lengths on and around its 32-key tiles and its
+    query blocks, N_q != N_k (both ways), head sharing, both head sizes,
+    causal or not."""
+    rng = np.random.default_rng(seed)
+    edges = [1, 2, 15, 16, 17, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 257]
+    cases = []
+    for _ in range(n):
+        n_q = int(rng.choice(edges)) if rng.random() < 0.6 else int(rng.integers(1, 400))
+        n_k = int(rng.choice(edges)) if rng.random() < 0.6 else int(rng.integers(1, 400))
+        h_kv = int(rng.choice([1, 2, 3]))
+        rep = int(rng.choice([1, 2, 4]))
+        cases.append((int(rng.integers(1, 3)), h_kv * rep, h_kv, n_q, n_k, int(rng.choice([64, 128])),
+                      bool(rng.random() < 0.6)))
+    return cases
+
+
+@pytest.mark.parametrize("case", _random_f32_cases(12), ids=lambda c: "x".join(str(x) for x in c))
+def test_fwd_f32_random_shapes(case):
+    spec = _spec(*case, dtype="f32", seed=43)
+    say(f"fa_fwd_f32 random {spec.name}")
+    data = inputs.prefill_inputs(spec)
+    o, lse = _run_fwd(data)
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, spec.causal)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, F32_TOL, F32_TOL, lse_relative=False, label=spec.name)
+
+
 # ------------------------------------------------------------------ sliding window
 WINDOW_BF16 = [
     # B, H, H_kv, N_q, N_k, d, window
