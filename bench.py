@@ -1,21 +1,37 @@
 #!/usr/bin/env python3
 """Benchmark of the attention hot path on one MI355X.
 
-One step = one pass of the whole path over one batch of synthetic input:
-  * prefill: fa_fwd on the MHA workload B=8, H=H_kv=32, N=2048, d=128, causal,
-    bf16 (the headline: attention TFLOP/s, FLOPs = 4*B*H*N_q*N_k*d halved for
-    causal);
-  * decode: fa_decode on the GQA decode workload B=32, H=32, H_kv=8, d=128,
-    seq lens uniform in [8192, 32768], 16 splits (KV-read GB/s).
-Inputs are resident in HBM before the timed region; outputs are preallocated.
-Each launch is bracketed by HIP events recorded on the stream it runs on.
+Every figure is timed on inputs resident in HBM with preallocated outputs;
+each launch is bracketed by HIP events recorded on the stream it runs on (the
+current stream, which the binding passes to the library).
 
-Prints ONE JSON line.  ``--workload`` swaps the prefill workload for another
-named one (for exploration; the headline is the default).
+Headline (``value``, ``roofline``): fa_fwd on the largest prefill workload,
+MQA B=4, H=64, H_kv=1, N=4096, d=128, non-causal, bf16 -- one step is one
+launch, launched back to back (nothing else on the device between launches).
+Attention TFLOP/s = 4*B*H*N_q*N_k*d (halved for causal) / launch time.
+
+Beside it, each timed the same way (back to back, its own roofline):
+  * ``prefill``: the GQA (B=1, H=32, H_kv=8, N=8192, causal, K x 2) and MHA
+    (B=8, H=32, N=2048, causal) workloads, and the headline again;
+  * ``decode``: fa_decode on B=32, H=32, H_kv=8, d=128, lengths uniform in
+    [8192, 32768], 16 splits (KV-read GB/s against the HBM peak);
+  * ``interleaved_step`` (secondary): each MHA prefill launch alternating with
+    a decode step, the step of the earlier benchmark;
+  * ``next``: sliding-window and chunked prefill, windowed, paged and FP8 decode.
+
+Clock: right after every timed launch (outside its events) a probe kernel
+samples the shader clock on each XCD; each row reports the observed clock and
+its fraction of the matrix-core peak at that clock beside the 2.4 GHz one.
+
+CPU baseline: the fp64 oracle on one of the headline's four sequences, timed
+on the host cores and compared element by element with the GPU output.
+
+Prints ONE JSON line.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import re
 import json
@@ -27,6 +43,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
+PEAK_CLOCK_GHZ = 2.4
+PROBE_TICKS = 300            # 3 us of the 100 MHz counter per probe
+PROBE_WORKGROUPS = 8         # one per XCD (workgroups go to the XCDs round robin)
 
 
 def parse():
@@ -34,14 +53,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="mha", choices=["mha", "gqa", "mqa"])
+    ap.add_argument("--workload", default="mqa", choices=["mha", "gqa", "mqa"],
+                    help="the prefill workload of --only prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-next", action="store_true",
-                    help="skip the sliding-window and chunked-prefill measurements (the 'next' object)")
-    ap.add_argument("--only", choices=["prefill", "decode", "next", "copy"], default=None,
-                    help="time one part only (for profiling runs): one half of the step, the 'next' "
-                         "workloads, or 'copy', a plain 1 GiB device-to-device copy (the reference for "
-                         "scaling HBM byte counters)")
+                    help="skip the sliding-window, chunked, paged and FP8 measurements (the 'next' object)")
+    ap.add_argument("--only", choices=["prefill", "decode", "step", "next", "copy"], default=None,
+                    help="time one part only (for profiling runs): one prefill workload back to back, the "
+                         "decode step, the interleaved MHA prefill + decode step, the 'next' workloads, or "
+                         "'copy', a plain 1 GiB device-to-device copy (the reference for scaling HBM byte "
+                         "counters)")
     return ap.parse_args()
 
 
@@ -90,23 +111,34 @@ def counters_for(kernel_key, src_files):
     return out or None
 
 
-def cpu_baseline(spec, n_batches):
+def cpu_baseline(spec, n_batches, o_gpu=None, lse_gpu=None):
     """The fp64 oracle on a bounded sample (the first n_batches sequences) of the
-    prefill workload, timed on the host cores."""
+    prefill workload, timed on the host cores; when the GPU output of the same
+    workload is given, its first n_batches sequences are compared with the
+    oracle's element by element (max |dO| and the lse error of the parity bar)."""
+    import numpy as np
     import oracle
     from transformer_attention_fa_amd import inputs, roofline
     import dataclasses
-    sub = dataclasses.replace(spec, B=n_batches)
+    sub = dataclasses.replace(spec, B=n_batches)      # blocks are seeded per (tensor, batch, head)
     data = inputs.prefill_inputs(sub)
     t0 = time.perf_counter()
-    oracle.attention(data.q, data.k, data.v, sub.scale, sub.causal)
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, sub.scale, sub.causal)
     dt = time.perf_counter() - t0
     flops = roofline.attention_flops(sub.B, sub.H, sub.N_q, sub.N_k, sub.d, sub.causal)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": (f"the whole {spec.name} workload" if n_batches == spec.B else
-                       f"{n_batches} of {spec.B} sequences ({n_batches * spec.H} heads) of {spec.name}")
-                      + f", fp64, {dt:.2f} s wall",
-            "cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
+    rec = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": (f"the whole {spec.name} workload" if n_batches == spec.B else
+                      f"{n_batches} of {spec.B} sequences ({n_batches * spec.H} heads x {spec.N_q} rows) of "
+                      f"{spec.name}") + f", fp64, {dt:.2f} s wall",
+           "cpu_count": os.cpu_count(), "cpu_model": cpu_model()}
+    if o_gpu is not None:
+        import torch
+        o = o_gpu[:n_batches].to(torch.float64).cpu().numpy()
+        lse = lse_gpu[:n_batches].to(torch.float64).cpu().numpy()
+        rec["parity"] = {"max_abs_dO": float(np.max(np.abs(o - o_ref))),
+                         "max_lse_err_rel_floor1": float(np.max(np.abs(lse - lse_ref) / np.maximum(np.abs(lse_ref), 1.0))),
+                         "tolerance": {"O": 2e-2, "lse": 1e-3}, "elements": int(o.size)}
+    return rec
 
 
 def cpu_model():
@@ -122,130 +154,308 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
-def time_launches(fn, steps, warmup):
-    """Average / median / min of `steps` launches (HIP events on the current stream), in ms."""
+class ClockProbe:
+    """Shader-clock samples taken right after timed launches (libfa_clock.so:
+    one single-wave workgroup per XCD reads the shader-cycle and 100 MHz
+    counters over PROBE_TICKS ticks)."""
+
+    def __init__(self, device, capacity):
+        import torch
+        from transformer_attention_fa_amd import build
+        self.lib = ctypes.CDLL(build.PROBE_LIB)
+        self.lib.fa_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        self.lib.fa_clock_probe.restype = ctypes.c_int
+        self.buf = torch.zeros((capacity, PROBE_WORKGROUPS, 4), dtype=torch.int64, device=device)
+        self.device = device
+        self.n = 0
+
+    def reset(self):
+        self.n = 0
+
+    def sample(self):
+        import torch
+        if self.n >= self.buf.shape[0]:
+            return
+        st = self.lib.fa_clock_probe(self.buf[self.n].data_ptr(), PROBE_WORKGROUPS, PROBE_TICKS,
+                                     torch.cuda.current_stream(self.device).cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"fa_clock_probe failed ({st})")
+        self.n += 1
+
+    def summary(self):
+        """Clock over the samples since reset (call after a synchronize)."""
+        import numpy as np
+        if self.n == 0:
+            return None
+        rec = self.buf[:self.n].cpu().numpy()
+        cyc, ticks, xcc = rec[..., 0].astype(np.float64), rec[..., 1].astype(np.float64), rec[..., 2]
+        per_sample = cyc.sum(axis=1) / ticks.sum(axis=1) * 0.1           # GHz (100 MHz ticks)
+        per_xcd = {}
+        for x in sorted(set(int(v) for v in xcc.ravel())):
+            m = xcc == x
+            per_xcd[str(x)] = round(float(np.median(cyc[m] / ticks[m] * 0.1)), 4)
+        return {"ghz_median": round(float(np.median(per_sample)), 4), "ghz_min": round(float(per_sample.min()), 4),
+                "ghz_max": round(float(per_sample.max()), 4), "ghz_median_per_xcd": per_xcd, "samples": self.n,
+                "method": f"s_memtime / s_memrealtime over {PROBE_TICKS} ticks of 100 MHz, one wave per XCD, "
+                          "right after each timed launch"}
+
+
+def time_launches(fn, steps, warmup, probe=None):
+    """Per-launch times (ms) of `steps` launches back to back, each bracketed by
+    HIP events on the current stream, a clock probe after each (outside the
+    events).  Returns (times, wall seconds of the timed loop, clock summary)."""
     import numpy as np
     import torch
     for _ in range(warmup):
         fn()
+        if probe is not None:
+            probe.sample()
+    torch.cuda.synchronize()
+    if probe is not None:
+        probe.reset()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
     for a, b in ev:
         a.record()
         fn()
         b.record()
+        if probe is not None:
+            probe.sample()
     torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
     t = np.array([a.elapsed_time(b) for a, b in ev])
-    return float(t.mean()), float(np.median(t)), float(t.min())
+    return t, wall, (probe.summary() if probe is not None else None)
 
 
-def measure_next(dev_bf16, steps, warmup, decode_state=None):
-    """The sliding-window, chunked-prefill and paged-cache rows, each on its own workload."""
+def stats(t):
+    import numpy as np
+    return {"ms_avg": float(np.mean(t)), "ms_median": float(np.median(t)), "ms_min": float(np.min(t))}
+
+
+def mfma_roofline(tflops, key, clock):
+    """Roofline object of a prefill row: the matrix-core bound, with the committed
+    counter figures while the kernel source matches them."""
+    from transformer_attention_fa_amd import roofline
+    r = {"bound": "mfma", "achieved": tflops, "peak": roofline.PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+         "frac": tflops / roofline.PEAK_BF16_TFLOPS, "traffic": traffic_for(f"fwd_bf16:{key}", ["fwd_bf16.hip"]),
+         "kernel": "fwd_bf16_kernel", "counters": counters_for(f"fwd_bf16:{key}", ["fwd_bf16.hip"])}
+    if clock:
+        peak_at = roofline.PEAK_BF16_TFLOPS * clock["ghz_median"] / PEAK_CLOCK_GHZ
+        r["clock"] = clock
+        r["peak_at_observed_clock"] = peak_at
+        r["frac_at_observed_clock"] = tflops / peak_at
+    return r
+
+
+def hbm_roofline(gbps, key, clock=None):
+    from transformer_attention_fa_amd import roofline
+    r = {"bound": "hbm", "achieved": gbps, "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
+         "frac": gbps / roofline.PEAK_HBM_GBPS, "traffic": traffic_for(f"decode:{key}", ["decode.hip"]),
+         "kernel": "decode_split_kernel + decode_combine_kernel",
+         "counters": counters_for(f"decode:{key}", ["decode.hip"])}
+    if clock:
+        r["clock"] = clock
+    return r
+
+
+def dev_bf16(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class PrefillRun:
+    """A prefill workload on the device: inputs, preallocated outputs, one launch."""
+
+    def __init__(self, spec, dev):
+        import torch
+        from transformer_attention_fa_amd import inputs
+        self.spec = spec
+        data = inputs.prefill_inputs(spec)
+        self.q, self.k, self.v = (dev_bf16(x, dev) for x in (data.q, data.k, data.v))
+        del data
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((spec.B, spec.H, spec.N_q), dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        from transformer_attention_fa_amd import api
+        s = self.spec
+        api.fwd(self.q, self.k, self.v, causal=s.causal, scale=s.scale, out=self.o, lse=self.lse,
+                window=s.window or None)
+
+    def free_inputs(self):
+        del self.q, self.k, self.v
+
+
+def prefill_row(run, steps, warmup, probe):
+    """One prefill workload timed back to back: TFLOP/s and its roofline."""
+    spec = run.spec
+    t, wall, clock = time_launches(run, steps, warmup, probe)
+    st = stats(t)
+    flops = spec.flops()
+    tflops = flops / (st["ms_avg"] * 1e-3) / 1e12
+    row = {"entry": "fa_fwd_window" if spec.window else "fa_fwd", "value": tflops, "unit": "TFLOP/s",
+           "timing": "back to back", **st, "wall_ms_per_launch": wall / steps * 1e3, "flop_per_launch": flops,
+           # exponentials per launch (one per visible score): the VALU /
+           # transcendental budget beside the matrix-core work
+           "exp_per_launch": flops / (4 * spec.d),
+           "shape": {"B": spec.B, "H": spec.H, "H_kv": spec.H_kv, "N_q": spec.N_q, "N_k": spec.N_k, "d": spec.d,
+                     "causal": spec.causal, "window": spec.window, "k_scale": spec.k_scale, "seed": spec.seed}}
+    row["roofline"] = mfma_roofline(tflops, spec.name, clock)
+    return row
+
+
+class DecodeRun:
+    """The decode workload on the device (caches, lengths, outputs, workspace)."""
+
+    def __init__(self, spec, dev):
+        import torch
+        from transformer_attention_fa_amd import api, inputs
+        self.spec = spec
+        data = inputs.decode_inputs(spec)
+        self.q = dev_bf16(data.q, dev)
+        self.kc, self.vc = dev_bf16(data.k_cache, dev), dev_bf16(data.v_cache, dev)
+        self.lens = torch.from_numpy(data.seq_lens).to(dev)
+        self.seq_lens = data.seq_lens.copy()
+        del data
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((spec.B, spec.H), dtype=torch.float32, device=dev)
+        self.ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits),
+                              dtype=torch.uint8, device=dev)
+
+    def __call__(self):
+        from transformer_attention_fa_amd import api
+        s = self.spec
+        api.decode(self.q, self.kc, self.vc, self.lens, num_splits=s.num_splits, scale=s.scale, out=self.o,
+                   lse=self.lse, workspace=self.ws)
+
+
+def decode_row(run, steps, warmup, probe=None):
+    from transformer_attention_fa_amd import roofline
+    spec = run.spec
+    t, wall, clock = time_launches(run, steps, warmup, probe)
+    st = stats(t)
+    kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, run.seq_lens)
+    gbps = kv / (st["ms_avg"] * 1e-3) / 1e9
+    return {"entry": "fa_decode", "value": gbps, "unit": "GB/s", "timing": "back to back", **st,
+            "wall_ms_per_launch": wall / steps * 1e3, "kv_bytes": kv,
+            "shape": {"B": spec.B, "H": spec.H, "H_kv": spec.H_kv, "d": spec.d,
+                      "seq_len_range": [spec.len_lo, spec.len_hi], "num_splits": spec.num_splits, "seed": spec.seed},
+            "roofline": hbm_roofline(gbps, spec.name, clock)}
+
+
+def interleaved_step(prun, drun, steps, warmup, probe):
+    """Secondary figure: each MHA prefill launch alternates with a decode step
+    (prefill and decode timed by their own events; the probe follows the
+    prefill launch)."""
+    import numpy as np
+    import torch
+    from transformer_attention_fa_amd import roofline
+    for _ in range(warmup):
+        prun()
+        drun()
+    torch.cuda.synchronize()
+    probe.reset()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in ev:
+        e[0].record()
+        prun()
+        e[1].record()
+        probe.sample()
+        e[2].record()
+        drun()
+        e[3].record()
+    torch.cuda.synchronize()
+    tp = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    td = np.array([e[2].elapsed_time(e[3]) for e in ev])
+    tf = prun.spec.flops() / (tp.mean() * 1e-3) / 1e12
+    kv = roofline.decode_kv_bytes(drun.spec.H_kv, drun.spec.d, drun.seq_lens)
+    return {"note": "secondary: each prefill launch alternates with a decode step; the memory-bound decode lets "
+                    "the clock recover between prefill launches",
+            "prefill": {"workload": prun.spec.name, "value": tf, "unit": "TFLOP/s", **stats(tp),
+                        "frac": tf / roofline.PEAK_BF16_TFLOPS, "clock": probe.summary()},
+            "decode": {"workload": drun.spec.name, "value": kv / (td.mean() * 1e-3) / 1e9, "unit": "GB/s",
+                       **stats(td)}}
+
+
+def measure_next(dev, steps, warmup, probe, drun=None):
+    """The sliding-window, chunked-prefill, windowed, paged and FP8 decode rows,
+    each on its own workload, back to back."""
     import numpy as np
     import torch
     from transformer_attention_fa_amd import api, inputs, roofline
     out = {}
     for spec in (inputs.SWA_PREFILL, inputs.CHUNKED_PREFILL):
-        data = inputs.prefill_inputs(spec)
-        q, k, v = (dev_bf16(x) for x in (data.q, data.k, data.v))
-        del data
-        o = torch.empty_like(q)
-        lse = torch.empty((spec.B, spec.H, spec.N_q), dtype=torch.float32, device=q.device)
-        win = spec.window or None
-        avg, med, mn = time_launches(lambda: api.fwd(q, k, v, causal=spec.causal, scale=spec.scale, out=o, lse=lse,
-                                                     window=win), steps, warmup)
-        flops = spec.flops()
-        tf = flops / (avg * 1e-3) / 1e12
-        out[spec.name] = {"entry": "fa_fwd_window" if win else "fa_fwd", "value": tf, "unit": "TFLOP/s",
-                          "frac_mfma_peak": tf / roofline.PEAK_BF16_TFLOPS, "ms_avg": avg, "ms_median": med,
-                          "ms_min": mn, "flop_per_launch": flops, "exp_per_launch": flops / (4 * spec.d),
-                          "window": spec.window,
-                          "shape": {"B": spec.B, "H": spec.H, "H_kv": spec.H_kv, "N_q": spec.N_q, "N_k": spec.N_k,
-                                    "d": spec.d, "causal": spec.causal}}
-        del q, k, v, o, lse
-    if decode_state is not None:
-        spec = inputs.SWA_DECODE
-        dq, kc, vc, lens, seq_lens, base = decode_state
-        assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
-        ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
-                         device=dq.device)
-        d_o = torch.empty_like(dq)
-        d_lse = torch.empty((spec.B, spec.H), dtype=torch.float32, device=dq.device)
-        avg, med, mn = time_launches(lambda: api.decode(dq, kc, vc, lens, num_splits=spec.num_splits,
-                                                        scale=spec.scale, out=d_o, lse=d_lse, workspace=ws,
-                                                        window=spec.window), steps, warmup)
-        kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, [min(int(n), spec.window) for n in seq_lens])
-        gbps = kv / (avg * 1e-3) / 1e9
-        out[spec.name] = {"entry": "fa_decode_window", "value": gbps, "unit": "GB/s",
-                          "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS, "ms_avg": avg, "ms_median": med,
-                          "ms_min": mn, "kv_bytes": kv, "window": spec.window, "num_splits": spec.num_splits}
-        # paged cache: the same rows dealt onto shuffled 16-row pages of a pool
-        spec = inputs.PAGED_DECODE
-        assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
-        table, num_pages = inputs.page_table(seq_lens, spec.page_size, spec.seed)
-        ps = spec.page_size
-        b_idx = np.concatenate([np.full(int(n), b) for b, n in enumerate(seq_lens)])
-        r_idx = np.concatenate([np.arange(int(n)) for n in seq_lens])
-        page_idx = torch.from_numpy(table[b_idx, r_idx // ps].astype(np.int64)).to(dq.device)
-        slot_idx = torch.from_numpy(r_idx % ps).to(dq.device)
-        bi, ri = torch.from_numpy(b_idx).to(dq.device), torch.from_numpy(r_idx).to(dq.device)
-        pools = []
-        for cache in (kc, vc):
-            pool = torch.zeros((num_pages, spec.H_kv, ps, spec.d), dtype=cache.dtype, device=dq.device)
-            pool[page_idx, :, slot_idx] = cache[bi, :, ri]
-            pools.append(pool)
-        del page_idx, slot_idx, bi, ri
-        bt = torch.from_numpy(np.maximum(table, 0)).to(dq.device)
-        ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
-                         device=dq.device)
-        avg, med, mn = time_launches(lambda: api.decode_paged(dq, pools[0], pools[1], bt, lens,
-                                                              num_splits=spec.num_splits, scale=spec.scale, out=d_o,
-                                                              lse=d_lse, workspace=ws), steps, warmup)
-        kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, seq_lens)
-        gbps = kv / (avg * 1e-3) / 1e9
-        out[spec.name] = {"entry": "fa_decode_paged", "value": gbps, "unit": "GB/s",
-                          "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS, "ms_avg": avg, "ms_median": med,
-                          "ms_min": mn, "kv_bytes": kv, "page_size": ps, "num_pages": num_pages,
-                          "num_splits": spec.num_splits}
-        del pools
-        # FP8 E4M3 cache: the same rows quantised per tensor on the device
-        spec = inputs.FP8_DECODE
-        assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
-        codes = []
-        for cache, sc in ((kc, spec.k_scale), (vc, spec.v_scale)):
-            x = (cache.float() * (1.0 / sc)).clamp_(-448.0, 448.0)
-            codes.append(x.to(torch.float8_e4m3fn).view(torch.uint8))
-            del x
-        ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
-                         device=dq.device)
-        avg, med, mn = time_launches(lambda: api.decode_fp8(dq, codes[0], codes[1], spec.k_scale, spec.v_scale, lens,
-                                                            num_splits=spec.num_splits, scale=spec.scale, out=d_o,
-                                                            lse=d_lse, workspace=ws), steps, warmup)
-        kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, seq_lens, elem=1)
-        gbps = kv / (avg * 1e-3) / 1e9
-        out[spec.name] = {"entry": "fa_decode_fp8", "value": gbps, "unit": "GB/s",
-                          "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS, "ms_avg": avg, "ms_median": med,
-                          "ms_min": mn, "kv_bytes": kv, "kv_format": "e4m3, per-tensor scales",
-                          "bf16_equivalent_GBps": 2 * gbps, "num_splits": spec.num_splits}
-        del codes
+        run = PrefillRun(spec, dev)
+        out[spec.name] = prefill_row(run, steps, warmup, probe)
+        del run
+    if drun is None:
+        return out
+    base = drun.spec
+    dq, kc, vc, lens, seq_lens = drun.q, drun.kc, drun.vc, drun.lens, drun.seq_lens
+    d_o, d_lse = drun.o, drun.lse
+
+    def dec_row(entry, fn, kv, spec, **extra):
+        t, wall, _ = time_launches(fn, steps, warmup)
+        st = stats(t)
+        gbps = kv / (st["ms_avg"] * 1e-3) / 1e9
+        return {"entry": entry, "value": gbps, "unit": "GB/s", "timing": "back to back", **st, "kv_bytes": kv,
+                "num_splits": spec.num_splits, **extra, "roofline": hbm_roofline(gbps, spec.name)}
+
+    spec = inputs.SWA_DECODE
+    assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
+    ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
+                     device=dev)
+    out[spec.name] = dec_row(
+        "fa_decode_window",
+        lambda: api.decode(dq, kc, vc, lens, num_splits=spec.num_splits, scale=spec.scale, out=d_o, lse=d_lse,
+                           workspace=ws, window=spec.window),
+        roofline.decode_kv_bytes(spec.H_kv, spec.d, [min(int(n), spec.window) for n in seq_lens]), spec,
+        window=spec.window)
+    # paged cache: the same rows dealt onto shuffled 16-row pages of a pool
+    spec = inputs.PAGED_DECODE
+    assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
+    table, num_pages = inputs.page_table(seq_lens, spec.page_size, spec.seed)
+    ps = spec.page_size
+    b_idx = np.concatenate([np.full(int(n), b) for b, n in enumerate(seq_lens)])
+    r_idx = np.concatenate([np.arange(int(n)) for n in seq_lens])
+    page_idx = torch.from_numpy(table[b_idx, r_idx // ps].astype(np.int64)).to(dev)
+    slot_idx = torch.from_numpy(r_idx % ps).to(dev)
+    bi, ri = torch.from_numpy(b_idx).to(dev), torch.from_numpy(r_idx).to(dev)
+    pools = []
+    for cache in (kc, vc):
+        pool = torch.zeros((num_pages, spec.H_kv, ps, spec.d), dtype=cache.dtype, device=dev)
+        pool[page_idx, :, slot_idx] = cache[bi, :, ri]
+        pools.append(pool)
+    del page_idx, slot_idx, bi, ri
+    bt = torch.from_numpy(np.maximum(table, 0)).to(dev)
+    ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
+                     device=dev)
+    out[spec.name] = dec_row(
+        "fa_decode_paged",
+        lambda: api.decode_paged(dq, pools[0], pools[1], bt, lens, num_splits=spec.num_splits, scale=spec.scale,
+                                 out=d_o, lse=d_lse, workspace=ws),
+        roofline.decode_kv_bytes(spec.H_kv, spec.d, seq_lens), spec, page_size=ps, num_pages=num_pages)
+    del pools
+    # FP8 E4M3 cache: the same rows quantised per tensor on the device
+    spec = inputs.FP8_DECODE
+    assert (spec.B, spec.H, spec.H_kv, spec.d, spec.seed) == (base.B, base.H, base.H_kv, base.d, base.seed)
+    codes = []
+    for cache, sc in ((kc, spec.k_scale), (vc, spec.v_scale)):
+        x = (cache.float() * (1.0 / sc)).clamp_(-448.0, 448.0)
+        codes.append(x.to(torch.float8_e4m3fn).view(torch.uint8))
+        del x
+    ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
+                     device=dev)
+    r = dec_row(
+        "fa_decode_fp8",
+        lambda: api.decode_fp8(dq, codes[0], codes[1], spec.k_scale, spec.v_scale, lens, num_splits=spec.num_splits,
+                               scale=spec.scale, out=d_o, lse=d_lse, workspace=ws),
+        roofline.decode_kv_bytes(spec.H_kv, spec.d, seq_lens, elem=1), spec, kv_format="e4m3, per-tensor scales")
+    r["bf16_equivalent_GBps"] = 2 * r["value"]
+    out[spec.name] = r
+    del codes
     return out
-
-
-def add_rooflines(nxt):
-    """Roofline objects for the 'next' entries (traffic from the committed counters when current)."""
-    from transformer_attention_fa_amd import roofline
-    for name, r in nxt.items():
-        if r["unit"] == "TFLOP/s":
-            r["roofline"] = {"bound": "mfma", "achieved": r["value"], "peak": roofline.PEAK_BF16_TFLOPS,
-                             "unit": "TFLOP/s", "frac": r["value"] / roofline.PEAK_BF16_TFLOPS,
-                             "traffic": traffic_for(f"fwd_bf16:{name}", ["fwd_bf16.hip"]), "kernel": "fwd_bf16_kernel",
-                             "counters": counters_for(f"fwd_bf16:{name}", ["fwd_bf16.hip"])}
-        else:
-            r["roofline"] = {"bound": "hbm", "achieved": r["value"], "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
-                             "frac": r["value"] / roofline.PEAK_HBM_GBPS,
-                             "traffic": traffic_for(f"decode:{name}", ["decode.hip"]),
-                             "kernel": "decode_split_kernel + decode_combine_kernel",
-                             "counters": counters_for(f"decode:{name}", ["decode.hip"])}
-    return nxt
 
 
 def main():
@@ -255,7 +465,6 @@ def main():
               "(each GPU would run its own shard of heads or sequences).", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
     from transformer_attention_fa_amd import api, inputs, roofline
 
@@ -271,114 +480,66 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.warmup + args.steps}))
         return
-    pspec = {"mha": inputs.MHA_PREFILL, "gqa": inputs.GQA_PREFILL, "mqa": inputs.MQA_PREFILL}[args.workload]
-    dspec = inputs.GQA_DECODE
-    do_prefill = args.only in (None, "prefill")
-    do_decode = args.only in (None, "decode", "next")     # 'next' reuses the decode caches
-
-    def dev_bf16(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
-
-    if do_prefill:
-        pdata = inputs.prefill_inputs(pspec)
-        q, k, v = (dev_bf16(x) for x in (pdata.q, pdata.k, pdata.v))
-        del pdata
-        o = torch.empty_like(q)
-        lse = torch.empty((pspec.B, pspec.H, pspec.N_q), dtype=torch.float32, device=dev)
-    if do_decode:
-        ddata = inputs.decode_inputs(dspec)
-        dq = dev_bf16(ddata.q)
-        kc, vc = dev_bf16(ddata.k_cache), dev_bf16(ddata.v_cache)
-        lens = torch.from_numpy(ddata.seq_lens).to(dev)
-        seq_lens = ddata.seq_lens.copy()
-        del ddata
-        d_o = torch.empty_like(dq)
-        d_lse = torch.empty((dspec.B, dspec.H), dtype=torch.float32, device=dev)
-        ws = torch.empty(api.decode_workspace_bytes(dspec.B, dspec.H, dspec.d, dspec.num_splits),
-                         dtype=torch.uint8, device=dev)
-
-    def step(ev=None):
-        if do_prefill:
-            if ev is not None:
-                ev[0].record()
-            api.fwd(q, k, v, causal=pspec.causal, scale=pspec.scale, out=o, lse=lse)
-            if ev is not None:
-                ev[1].record()
-        if do_decode:
-            if ev is not None:
-                ev[2].record()
-            api.decode(dq, kc, vc, lens, num_splits=dspec.num_splits, scale=dspec.scale,
-                       out=d_o, lse=d_lse, workspace=ws)
-            if ev is not None:
-                ev[3].record()
-
-    if args.only == "next":
-        rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-               "next": add_rooflines(measure_next(dev_bf16, args.steps, args.warmup,
-                                                  (dq, kc, vc, lens, seq_lens, dspec)))}
-        print(json.dumps(rec), flush=True)
-        return
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    rec = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
-           "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)"}
-    config = {"workload": "", "prefill": None, "decode": None}
-    if do_prefill:
-        t_pf = [e[0].elapsed_time(e[1]) for e in events]        # ms
-        t_avg = float(np.mean(t_pf))
-        flops = pspec.flops()
-        tflops = flops / (t_avg * 1e-3) / 1e12
-        traffic = traffic_for(f"fwd_bf16:{pspec.name}", ["fwd_bf16.hip"])
-        rec.update({"value": tflops, "unit": "TFLOP/s"})
-        rec["roofline"] = {"bound": "mfma", "achieved": tflops, "peak": roofline.PEAK_BF16_TFLOPS,
-                           "unit": "TFLOP/s", "frac": tflops / roofline.PEAK_BF16_TFLOPS, "traffic": traffic,
-                           "kernel": "fwd_bf16_kernel", "launch_ms_avg": t_avg,
-                           "launch_ms_median": float(np.median(t_pf)), "launch_ms_min": float(np.min(t_pf)),
-                           "flop_per_launch": flops,
-                           # exponentials per launch (one per visible score): the VALU /
-                           # transcendental budget beside the MFMA work
-                           "exp_per_launch": flops / (4 * pspec.d),
-                           "counters": counters_for(f"fwd_bf16:{pspec.name}", ["fwd_bf16.hip"])}
-        config["workload"] = pspec.name
-        config["prefill"] = {"B": pspec.B, "H": pspec.H, "H_kv": pspec.H_kv, "N_q": pspec.N_q, "N_k": pspec.N_k,
-                             "d": pspec.d, "causal": pspec.causal, "seed": pspec.seed}
-    if do_decode:
-        t_dc = [e[2].elapsed_time(e[3]) for e in events]
-        t_avg_d = float(np.mean(t_dc))
-        kv_bytes = roofline.decode_kv_bytes(dspec.H_kv, dspec.d, seq_lens)
-        gbps = kv_bytes / (t_avg_d * 1e-3) / 1e9
-        rec["decode"] = {"value": gbps, "unit": "GB/s", "frac_hbm_peak": gbps / roofline.PEAK_HBM_GBPS,
-                         "ms_avg": t_avg_d, "ms_median": float(np.median(t_dc)), "ms_min": float(np.min(t_dc)),
-                         "kv_bytes": kv_bytes,
-                         "roofline": {"bound": "hbm", "achieved": gbps, "peak": roofline.PEAK_HBM_GBPS,
-                                      "unit": "GB/s", "frac": gbps / roofline.PEAK_HBM_GBPS,
-                                      "traffic": traffic_for(f"decode:{dspec.name}", ["decode.hip"]),
-                                      "kernel": "decode_split_kernel + decode_combine_kernel",
-                                      "counters": counters_for(f"decode:{dspec.name}", ["decode.hip"])}}
-        config["workload"] = (config["workload"] + " + " if config["workload"] else "") + dspec.name
-        config["decode"] = {"B": dspec.B, "H": dspec.H, "H_kv": dspec.H_kv, "d": dspec.d,
-                            "seq_len_range": [dspec.len_lo, dspec.len_hi], "num_splits": dspec.num_splits,
-                            "seed": dspec.seed}
-        if not do_prefill:
-            rec.update({"value": gbps, "unit": "GB/s"})
-    rec["config"] = config
-    if args.only is None and not args.no_next:
-        rec["next"] = add_rooflines(measure_next(dev_bf16, args.steps, args.warmup,
-                                                 (dq, kc, vc, lens, seq_lens, dspec) if do_decode else None))
-    if do_prefill and not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(pspec, n_batches=pspec.B)
+    probe = ClockProbe(dev, max(args.steps, args.warmup))
+    base = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)"}
     props = torch.cuda.get_device_properties(dev)
-    rec["device"] = {"name": props.name, "cus": props.multi_processor_count,
-                     "gcn_arch": getattr(props, "gcnArchName", "")}
+    device = {"name": props.name, "cus": props.multi_processor_count, "gcn_arch": getattr(props, "gcnArchName", "")}
+
+    if args.only == "prefill":
+        spec = {"mha": inputs.MHA_PREFILL, "gqa": inputs.GQA_PREFILL, "mqa": inputs.MQA_PREFILL}[args.workload]
+        row = prefill_row(PrefillRun(spec, dev), args.steps, args.warmup, probe)
+        print(json.dumps({**base, "value": row["value"], "unit": "TFLOP/s", "ms_per_step": row["wall_ms_per_launch"],
+                          "config": {"workload": spec.name, **row["shape"], "timing": "back to back"},
+                          "roofline": row["roofline"], "prefill": {spec.name: row}, "device": device}), flush=True)
+        return
+    if args.only == "decode":
+        row = decode_row(DecodeRun(inputs.GQA_DECODE, dev), args.steps, args.warmup, probe)
+        print(json.dumps({**base, "value": row["value"], "unit": "GB/s", "ms_per_step": row["wall_ms_per_launch"],
+                          "config": {"workload": inputs.GQA_DECODE.name, **row["shape"]}, "roofline": row["roofline"],
+                          "decode": row, "device": device}), flush=True)
+        return
+    if args.only == "step":
+        rec = interleaved_step(PrefillRun(inputs.MHA_PREFILL, dev), DecodeRun(inputs.GQA_DECODE, dev), args.steps,
+                               args.warmup, probe)
+        print(json.dumps({**base, "value": rec["prefill"]["value"], "unit": "TFLOP/s",
+                          "config": {"workload": inputs.MHA_PREFILL.name + " + " + inputs.GQA_DECODE.name},
+                          "interleaved_step": rec, "device": device}), flush=True)
+        return
+    if args.only == "next":
+        nxt = measure_next(dev, args.steps, args.warmup, probe, DecodeRun(inputs.GQA_DECODE, dev))
+        print(json.dumps({**base, "next": nxt, "device": device}), flush=True)
+        return
+
+    # ---- the default run
+    head_spec = inputs.MQA_PREFILL
+    head = PrefillRun(head_spec, dev)
+    head_row = prefill_row(head, args.steps, args.warmup, probe)
+    head.free_inputs()
+    rows = {head_spec.name: head_row}
+    for spec in (inputs.GQA_PREFILL, inputs.MHA_PREFILL):
+        run = PrefillRun(spec, dev)
+        rows[spec.name] = prefill_row(run, args.steps, args.warmup, probe)
+        if spec is inputs.MHA_PREFILL:
+            mha = run
+        else:
+            del run
+    drun = DecodeRun(inputs.GQA_DECODE, dev)
+    drow = decode_row(drun, args.steps, args.warmup, probe)
+    rec = {**base, "value": head_row["value"], "unit": "TFLOP/s", "ms_per_step": head_row["wall_ms_per_launch"],
+           "config": {"workload": head_spec.name, **head_row["shape"], "timing": "back to back"},
+           "roofline": {**head_row["roofline"], "launch_ms_avg": head_row["ms_avg"],
+                        "launch_ms_median": head_row["ms_median"], "launch_ms_min": head_row["ms_min"],
+                        "flop_per_launch": head_row["flop_per_launch"], "exp_per_launch": head_row["exp_per_launch"]},
+           "prefill": rows, "decode": drow,
+           "interleaved_step": interleaved_step(mha, drun, args.steps, args.warmup, probe)}
+    del mha
+    if not args.no_next:
+        rec["next"] = measure_next(dev, args.steps, args.warmup, probe, drun)
+    del drun
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(head_spec, 1, head.o, head.lse)
+    rec["device"] = device
     print(json.dumps(rec), flush=True)
 
 

@@ -52,13 +52,19 @@
  *    (FA_ERR_INVALID_ARGUMENT / FA_ERR_UNSUPPORTED) and nothing is written.
  *    A failed launch returns FA_ERR_HIP.  fa_last_error() gives a message for
  *    the calling thread's last failure.  Nothing throws across the ABI.
- *  - Sizes: each tensor may hold up to 2^40 elements (larger problems return
- *    FA_ERR_UNSUPPORTED); the kernels address memory with 64-bit offsets, so
- *    a tensor may span more than 4 GiB.
- *  - Thread safety: calls may come from any thread.  The process-wide state is
- *    the per-thread message, the workgroup cap of fa_fwd_set_max_workgroups
- *    (an atomic) and a per-device cache of how many prefill workgroups fit on
- *    the device (filled once, the same value by every thread).
+ *  - Sizes: each tensor may hold up to 2^40 elements; the kernels address
+ *    memory with 64-bit offsets, so a tensor may span more than 4 GiB.  The
+ *    launch grids bound a few counts further.  Each limit is checked on the
+ *    host and returns FA_ERR_UNSUPPORTED before any launch:
+ *      fa_fwd, fa_fwd_window:  B * H * ceil(N_q / 256) <= 2^31 - 1;
+ *      fa_fwd_f32:             B * H * ceil(N_q / 64)  <= 2^31 - 1 at d = 128,
+ *                              B * H * ceil(N_q / 128) <= 2^31 - 1 at d = 64;
+ *      decode entry points:    B <= 65535, H_kv * ceil((H / H_kv) / 16) <= 65535,
+ *                              B * H <= 2^31 - 4.
+ *  - Thread safety: calls may come from any thread and keep no setting
+ *    between calls.  The only process-wide state is the per-thread error
+ *    message and a per-device cache of how many prefill workgroups fit on the
+ *    device (filled once, the same value by every thread).
  */
 #ifndef FA_H
 #define FA_H
@@ -109,26 +115,21 @@ fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, 
                           float scale, int window, hipStream_t stream);
 
 /*
- * fa_fwd_f32 -- the same operation with fp32 inputs and fp32 output
- * (fp32 arithmetic throughout).  Arguments and semantics as fa_fwd.
+ * fa_fwd_f32 -- the same operation as fa_fwd with fp32 inputs and fp32
+ * output, fp32 arithmetic throughout [AV §3: tiles of Q, K and V with a
+ * running max and running sum per row give exactly the standard attention;
+ * AV §2 head sharing; AV §5.5 causal].  The path exists for precision, not
+ * speed: scores, exponentials and the output accumulate in fp32 from the
+ * stored fp32 values.
+ *   q      [B,H,N_q,d]    fp32, device
+ *   k, v   [B,H_kv,N_k,d] fp32, device
+ *   o      [B,H,N_q,d]    fp32, device, written
+ *   lse    [B,H,N_q]      fp32, device, written; may be NULL
+ * Other arguments, limits and errors as fa_fwd.
  */
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                        int B, int H, int H_kv, int N_q, int N_k, int d,
                        float scale, int causal, hipStream_t stream);
-
-/*
- * fa_fwd_set_max_workgroups -- a cap on the workgroups of the bf16 prefill
- * at d = 128 (fa_fwd, fa_fwd_window).  That kernel runs a persistent grid,
- * one workgroup per slot that fits on the device, each working through a
- * list of (query block, head, batch) items; the cap leaves compute units to
- * other work on the device, and a small cap makes every workgroup run many
- * items in a row.  It is a scheduling control, not part of the operation:
- * results are the same for every value.
- *   n = 0: no cap (the default); n >= 1: at most n workgroups.
- *   n < 0: FA_ERR_INVALID_ARGUMENT.
- * The setting is process-wide and applies to launches issued after the call.
- */
-fa_status_t fa_fwd_set_max_workgroups(int n);
 
 /*
  * fa_decode_workspace_bytes -- size of the workspace fa_decode needs:

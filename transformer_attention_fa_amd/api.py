@@ -23,7 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_fwd_set_max_workgroups", "fa_decode",
+EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode",
             "fa_decode_window", "fa_decode_paged", "fa_decode_fp8", "fa_decode_workspace_bytes",
             "fa_status_string", "fa_last_error")
 
@@ -63,8 +63,6 @@ def load():
     lib.fa_decode_paged.restype = i
     lib.fa_decode_fp8.argtypes = [vp, vp, vp, f, f, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode_fp8.restype = i
-    lib.fa_fwd_set_max_workgroups.argtypes = [i]
-    lib.fa_fwd_set_max_workgroups.restype = i
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
@@ -160,13 +158,35 @@ def fwd_f32(q, k, v, causal: bool = False, scale: float | None = None, out=None,
     return _fwd(load().fa_fwd_f32, torch.float32, q, k, v, causal, scale, out, lse)
 
 
-def fwd_set_max_workgroups(n: int) -> None:
-    """fa_fwd_set_max_workgroups: cap the persistent prefill grid (0 = no cap)."""
-    check(load().fa_fwd_set_max_workgroups(int(n)))
-
-
 def decode_workspace_bytes(B: int, H: int, d: int, num_splits: int) -> int:
     return int(load().fa_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def _decode_outputs(q, num_splits, out, lse, workspace):
+    """Workspace, o [B,H,d] (bf16) and lse [B,H] (fp32, or False for none) of a
+    decode call: allocated when not given, shape-checked when given (the
+    kernels write B*H rows of d values and B*H lse values)."""
+    torch = _torch()
+    B, H, d = q.shape
+    need = decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        # need == 0 means the arguments are invalid: the library call reports why
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    else:
+        _require(workspace, "workspace", torch.uint8, 1, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _require(out, "out", torch.bfloat16, 3, q.device)
+        if tuple(out.shape) != (B, H, d):
+            raise ValueError(f"out must have shape {(B, H, d)}, got {tuple(out.shape)}")
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    elif lse is not False:
+        _require(lse, "lse", torch.float32, 2, q.device)
+        if tuple(lse.shape) != (B, H):
+            raise ValueError(f"lse must have shape {(B, H)}, got {tuple(lse.shape)}")
+    return workspace, out, (None if lse is False else lse)
 
 
 def decode(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | None = None,
@@ -188,21 +208,7 @@ def decode(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | N
         raise ValueError("shape mismatch between q, caches and seq_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(B, H, d, num_splits)
-    if workspace is None:
-        # need == 0 means the arguments are invalid: the library call below reports why
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _require(workspace, "workspace", torch.uint8, 1, q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _require(out, "out", torch.bfloat16, 3, q.device)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    elif lse is not False:
-        _require(lse, "lse", torch.float32, 2, q.device)
-    lse_t = None if lse is False else lse
+    workspace, out, lse_t = _decode_outputs(q, num_splits, out, lse, workspace)
     with torch.cuda.device(q.device):
         if window is None:
             check(load().fa_decode(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
@@ -232,20 +238,7 @@ def decode_paged(q, k_pages, v_pages, block_table, seq_lens, num_splits: int = 1
         raise ValueError("shape mismatch between q, page pools, block_table and seq_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(B, H, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _require(workspace, "workspace", torch.uint8, 1, q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _require(out, "out", torch.bfloat16, 3, q.device)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    elif lse is not False:
-        _require(lse, "lse", torch.float32, 2, q.device)
-    lse_t = None if lse is False else lse
+    workspace, out, lse_t = _decode_outputs(q, num_splits, out, lse, workspace)
     with torch.cuda.device(q.device):
         check(load().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), block_table.data_ptr(),
                                      block_table.shape[1], seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t),
@@ -269,20 +262,7 @@ def decode_fp8(q, k_cache, v_cache, k_scale: float, v_scale: float, seq_lens, nu
         raise ValueError("shape mismatch between q, caches and seq_lens")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    need = decode_workspace_bytes(B, H, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
-        _require(workspace, "workspace", torch.uint8, 1, q.device)
-    if out is None:
-        out = torch.empty_like(q)
-    else:
-        _require(out, "out", torch.bfloat16, 3, q.device)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
-    elif lse is not False:
-        _require(lse, "lse", torch.float32, 2, q.device)
-    lse_t = None if lse is False else lse
+    workspace, out, lse_t = _decode_outputs(q, num_splits, out, lse, workspace)
     with torch.cuda.device(q.device):
         check(load().fa_decode_fp8(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), float(k_scale),
                                    float(v_scale), seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t), B, H, H_kv,

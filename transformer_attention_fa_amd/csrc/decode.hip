@@ -300,6 +300,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     constexpr int VSTAGE = 2 * 2 * TILEB;    // FP8: bf16 copy of the V tile, after the two stages
     constexpr int WAVE_LDS = 2 * 2 * TILEB + (KV8 ? TK * D * 2 : 0);
     static_assert(TILEB % (64 * 16) == 0, "tile shape");
+    static_assert(kDecodeHeadGroup == 16, "a workgroup serves up to 16 query heads (the 16x16 MFMA columns)");
 
     constexpr int QB = 16 * 256;             // Q rows of the head group (16 x 256 B at most)
     __shared__ __attribute__((aligned(1024))) char lds[NW * WAVE_LDS + QB];
@@ -660,14 +661,13 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     p.page_size = a.page_size;
     p.num_pages = a.num_pages;
     p.rep = a.H / a.H_kv;
-    p.ngrp = (p.rep + 15) / 16;               // groups of up to 16 query heads per KV head
+    p.ngrp = (p.rep + kDecodeHeadGroup - 1) / kDecodeHeadGroup;   // groups of up to 16 query heads per KV head
     const float sc = KV8 ? a.scale * a.k_scale : a.scale;   // FP8: keys are k_scale * code
     p.c = sc > 0.f ? sc * kLog2e : 1e-30f;
     p.v_scale = KV8 ? a.v_scale : 1.f;
     p.o = a.num_splits == 1 ? static_cast<uint16_t*>(a.o) : nullptr;
     p.lse = a.lse;
-    const long long gy = (long long)a.H_kv * p.ngrp;
-    if (gy > 65535 || a.B > 65535) return hipErrorInvalidConfiguration;
+    const long long gy = (long long)a.H_kv * p.ngrp;   // gy and B at most 65535: checked on the host
     hipLaunchKernelGGL((decode_split_kernel<D, PAGED, KV8>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1) return e;

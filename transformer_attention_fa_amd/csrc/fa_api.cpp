@@ -3,8 +3,8 @@
 // synchronisation, no exceptions across the boundary.
 #include "fa.h"
 #include "fa_internal.h"
+#include "fa_testing.h"
 
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdint>
@@ -14,9 +14,6 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
-
-// cap on the persistent prefill grid (fa_fwd_set_max_workgroups), 0 = none
-std::atomic<int> g_fwd_max_workgroups{0};
 
 fa_status_t fail(fa_status_t s, const char* fmt, ...)
 {
@@ -68,6 +65,18 @@ fa_status_t check_common(const void* q, const void* k, const void* v, const void
     return FA_OK;
 }
 
+// Grid limits of the prefill kernels: one work item (bf16) or workgroup (fp32)
+// per block of query rows of each (batch, head); HIP's grid holds at most
+// 2^31 - 1 workgroups in x.
+fa_status_t check_fwd_grid(int B, int H, int N_q, int rows_per_block, const char* name)
+{
+    const long long blocks = ((long long)N_q + rows_per_block - 1) / rows_per_block * (long long)H * (long long)B;
+    if (blocks > fa::kMaxGridX)
+        return fail(FA_ERR_UNSUPPORTED, "%s: %lld query blocks of %d rows (B*H*ceil(N_q/%d)) exceed the %lld "
+                    "workgroups of a launch", name, blocks, rows_per_block, rows_per_block, fa::kMaxGridX);
+    return FA_OK;
+}
+
 fa_status_t from_hip(hipError_t e, const char* what)
 {
     if (e == hipSuccess) return FA_OK;
@@ -94,6 +103,18 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
 {
     fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
     if (s != FA_OK) return s;
+    // grid limits: the split kernel runs (num_splits, H_kv * ceil(rep / 16),
+    // B) workgroups, the merge one workgroup per 4 (b, h) rows
+    const long long head_groups = (long long)H_kv * ((H / H_kv + fa::kDecodeHeadGroup - 1) / fa::kDecodeHeadGroup);
+    if (B > fa::kMaxGridYZ)
+        return fail(FA_ERR_UNSUPPORTED, "%s: B=%d sequences exceed the %lld a launch can take", name, B,
+                    fa::kMaxGridYZ);
+    if (head_groups > fa::kMaxGridYZ)
+        return fail(FA_ERR_UNSUPPORTED, "%s: H_kv * ceil((H/H_kv)/%d) = %lld head groups exceed the %lld a launch "
+                    "can take", name, fa::kDecodeHeadGroup, head_groups, fa::kMaxGridYZ);
+    if ((long long)B * H > fa::kMaxGridX - 3)
+        return fail(FA_ERR_UNSUPPORTED, "%s: B*H = %lld query rows exceed %lld", name, (long long)B * H,
+                    fa::kMaxGridX - 3);
     if (!seq_lens)
         return fail(FA_ERR_INVALID_ARGUMENT, "null seq_lens");
     if (!aligned(seq_lens, 4))
@@ -140,9 +161,9 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    float scale, int causal, hipStream_t stream)
 {
     fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
+    if (s == FA_OK) s = check_fwd_grid(B, H, N_q, fa::kFwdBf16Rows, "fa_fwd");
     if (s != FA_OK) return s;
     fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0, 0};
-    a.max_workgroups = g_fwd_max_workgroups.load(std::memory_order_relaxed);
     return from_hip(fa::launch_fwd_bf16(a, stream), "fa_fwd launch");
 }
 
@@ -151,19 +172,28 @@ fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, 
                           float scale, int window, hipStream_t stream)
 {
     fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
+    if (s == FA_OK) s = check_fwd_grid(B, H, N_q, fa::kFwdBf16Rows, "fa_fwd_window");
     if (s != FA_OK) return s;
     if (window < 1)
         return fail(FA_ERR_INVALID_ARGUMENT, "window=%d must be at least 1", window);
     fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, 1, window};
-    a.max_workgroups = g_fwd_max_workgroups.load(std::memory_order_relaxed);
     return from_hip(fa::launch_fwd_bf16(a, stream), "fa_fwd_window launch");
 }
 
-fa_status_t fa_fwd_set_max_workgroups(int n)
+fa_status_t fa_testing_fwd_capped(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int B, int H, int H_kv, int N_q, int N_k, int d, float scale, int causal,
+                                  int window, int max_workgroups, hipStream_t stream)
 {
-    if (n < 0) return fail(FA_ERR_INVALID_ARGUMENT, "fa_fwd_set_max_workgroups: n must be >= 0");
-    g_fwd_max_workgroups.store(n, std::memory_order_relaxed);
-    return FA_OK;
+    fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
+    if (s == FA_OK) s = check_fwd_grid(B, H, N_q, fa::kFwdBf16Rows, "fa_testing_fwd_capped");
+    if (s != FA_OK) return s;
+    if (window < 0 || (window > 0 && !causal))
+        return fail(FA_ERR_INVALID_ARGUMENT, "window=%d: 0 (none) or >= 1 with causal", window);
+    if (max_workgroups < 0)
+        return fail(FA_ERR_INVALID_ARGUMENT, "max_workgroups=%d must be >= 0", max_workgroups);
+    fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0, window};
+    a.max_workgroups = max_workgroups;
+    return from_hip(fa::launch_fwd_bf16(a, stream), "fa_testing_fwd_capped launch");
 }
 
 fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
@@ -171,6 +201,7 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                        float scale, int causal, hipStream_t stream)
 {
     fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
+    if (s == FA_OK) s = check_fwd_grid(B, H, N_q, fa::fwd_f32_rows(d), "fa_fwd_f32");
     if (s != FA_OK) return s;
     fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0, 0};
     return from_hip(fa::launch_fwd_f32(a, stream), "fa_fwd_f32 launch");

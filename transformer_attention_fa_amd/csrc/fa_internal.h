@@ -8,6 +8,16 @@
 
 namespace fa {
 
+// Launch geometry the host checks before any launch (the kernels assert that
+// they match): query rows per work item of the bf16 prefill, query rows per
+// workgroup of the fp32 prefill (by head size), query heads per decode
+// workgroup, and HIP's limits on grid sizes.
+constexpr int kFwdBf16Rows = 256;
+constexpr int fwd_f32_rows(int d) { return d == 128 ? 64 : 128; }
+constexpr int kDecodeHeadGroup = 16;
+constexpr long long kMaxGridX = 0x7fffffffLL;
+constexpr long long kMaxGridYZ = 65535;
+
 // One prefill problem, as validated by fa_fwd / fa_fwd_f32.
 struct FwdArgs {
     const void* q;       // [B,H,N_q,d]
@@ -19,7 +29,7 @@ struct FwdArgs {
     float scale;         // softmax scale on q.k
     int causal;
     int window;          // sliding window in keys (causal only), 0 = none
-    int max_workgroups = 0;   // cap on the persistent grid, 0 = none
+    int max_workgroups = 0;   // cap on the persistent grid, 0 = none (a test hook)
 };
 
 // One decode step, as validated by fa_decode.

@@ -779,6 +779,7 @@ template <int D, int NW, bool CAUSAL, bool PERSIST>
 hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
+    static_assert(BM == kFwdBf16Rows, "the host checks item counts with this block size");
     Params p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -797,8 +798,7 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     // scale 0 runs as a tiny positive scale: every exp2 argument then rounds to
     // 0 exactly as with scale 0, and masked scores stay -inf instead of NaN
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
-    const long long items = (long long)p.nqb * a.H * a.B;
-    if (items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const long long items = (long long)p.nqb * a.H * a.B;   // at most 2^31 - 1: checked on the host
     if (items == 0) return hipSuccess;
     long long grid = items;
     int xcd = 0;

@@ -158,6 +158,7 @@ template <int D, bool CAUSAL>
 hipError_t launch(const FwdArgs& a, hipStream_t stream)
 {
     constexpr int BM = 256 / (D / 32);
+    static_assert(BM == fwd_f32_rows(D), "the host checks workgroup counts with this block size");
     Params p;
     p.q = static_cast<const float*>(a.q);
     p.k = static_cast<const float*>(a.k);
@@ -172,8 +173,7 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream)
     p.rep = a.H / a.H_kv;
     p.nqb = (a.N_q + BM - 1) / BM;
     p.c = a.scale * kLog2e;
-    const long long blocks = (long long)p.nqb * a.H * a.B;
-    if (blocks > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const long long blocks = (long long)p.nqb * a.H * a.B;   // at most 2^31 - 1: checked on the host
     hipLaunchKernelGGL((fwd_f32_kernel<D, CAUSAL>), dim3((unsigned)blocks), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
