@@ -48,6 +48,11 @@ PROBE_TICKS = 300            # 3 us of the 100 MHz counter per probe
 PROBE_WORKGROUPS = 8         # one per XCD (workgroups go to the XCDs round robin)
 
 
+def log(msg):
+    """Progress on stderr (the JSON line is the only stdout output)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +125,7 @@ def cpu_baseline(spec, n_batches, o_gpu=None, lse_gpu=None):
     import oracle
     from transformer_attention_fa_amd import inputs, roofline
     import dataclasses
+    log(f"cpu baseline: the oracle on {n_batches} of {spec.B} sequences of {spec.name}")
     sub = dataclasses.replace(spec, B=n_batches)      # blocks are seeded per (tensor, batch, head)
     data = inputs.prefill_inputs(sub)
     t0 = time.perf_counter()
@@ -290,6 +296,7 @@ class PrefillRun:
 def prefill_row(run, steps, warmup, probe):
     """One prefill workload timed back to back: TFLOP/s and its roofline."""
     spec = run.spec
+    log(f"timing {spec.name}")
     t, wall, clock = time_launches(run, steps, warmup, probe)
     st = stats(t)
     flops = spec.flops()
@@ -312,6 +319,7 @@ class DecodeRun:
         import torch
         from transformer_attention_fa_amd import api, inputs
         self.spec = spec
+        log(f"drawing {spec.name}")
         data = inputs.decode_inputs(spec)
         self.q = dev_bf16(data.q, dev)
         self.kc, self.vc = dev_bf16(data.k_cache, dev), dev_bf16(data.v_cache, dev)
@@ -333,6 +341,7 @@ class DecodeRun:
 def decode_row(run, steps, warmup, probe=None):
     from transformer_attention_fa_amd import roofline
     spec = run.spec
+    log(f"timing {spec.name}")
     t, wall, clock = time_launches(run, steps, warmup, probe)
     st = stats(t)
     kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, run.seq_lens)
@@ -351,6 +360,7 @@ def interleaved_step(prun, drun, steps, warmup, probe):
     import numpy as np
     import torch
     from transformer_attention_fa_amd import roofline
+    log("timing the interleaved prefill + decode step")
     for _ in range(warmup):
         prun()
         drun()
@@ -396,6 +406,7 @@ def measure_next(dev, steps, warmup, probe, drun=None):
     d_o, d_lse = drun.o, drun.lse
 
     def dec_row(entry, fn, kv, spec, **extra):
+        log(f"timing {spec.name}")
         t, wall, _ = time_launches(fn, steps, warmup)
         st = stats(t)
         gbps = kv / (st["ms_avg"] * 1e-3) / 1e9
