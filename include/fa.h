@@ -177,6 +177,29 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
                       hipStream_t stream);
 
 /*
+ * fa_decode_noalloc -- fa_decode without a caller workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  It allocates nothing and calls no
+ * allocating routine.  The split partials go to a scratch array inside the
+ * library instead: 16 MiB (16777216 bytes) per GPU, one array per GPU the
+ * library runs on, held until the process ends.  Its address on a device is
+ * looked up on the first call with that device current.
+ *   The call needs fa_decode_workspace_bytes(B, H, d, num_splits) <= 16 MiB
+ *   (at d = 128 and 16 splits: B * H <= 2032); larger calls return
+ *   FA_ERR_UNSUPPORTED before any launch.
+ *   Every call on one GPU shares that GPU's array, and the array keeps the
+ *   last call's contents.  Each call writes every partial it reads before
+ *   reading it, so nothing needs clearing between calls.  Calls that overlap
+ *   on one GPU (on different streams, or from several threads) race on the
+ *   array: serialise them, or use fa_decode with a workspace per stream.
+ *   Other arguments, results and errors as fa_decode.
+ */
+fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int* seq_lens, void* o, float* lse,
+                              int B, int H, int H_kv, int N_max, int d, float scale,
+                              int num_splits, hipStream_t stream);
+
+/*
  * fa_decode_window -- fa_decode where the query sees only the last `window`
  * cached rows of its sequence, keys [max(0, seq_lens[b] - window),
  * seq_lens[b]) [AV §4 sliding window; for the newest token the window ends

@@ -289,3 +289,28 @@ def test_limits_apply_to_every_decode_entry(lib):
     assert lib.fa_decode_paged(a["q"], a["k"], a["v"], P, 1, a["lens"], a["o"], a["lse"], a["B"], a["H"],
                                a["H_kv"], 1, 16, a["d"], a["scale"], a["S"], a["ws"], a["ws_bytes"],
                                None) == UNSUPPORTED
+
+
+def _noalloc(lib, **change):
+    a = dict(GOOD_DEC, **change)
+    return lib.fa_decode_noalloc(a["q"], a["k"], a["v"], a["lens"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"],
+                                 a["N_max"], a["d"], a["scale"], a["S"], None)
+
+
+@pytest.mark.parametrize("name,change,expect",
+                         [c for c in DEC_CASES if not c[0].startswith("workspace")],
+                         ids=[c[0] for c in DEC_CASES if not c[0].startswith("workspace")])
+def test_decode_noalloc_rejects_before_launch(lib, name, change, expect):
+    st = _noalloc(lib, **change)
+    assert st == expect, (name, st, lib.fa_last_error())
+
+
+def test_decode_noalloc_scratch_limit(lib):
+    # partials of B*H*S*(d+1)*4 bytes (lse area 256-byte aligned) must fit 16 MiB
+    limit = 16 << 20
+    assert lib.fa_decode_workspace_bytes(2032, 1, 128, 16) <= limit < lib.fa_decode_workspace_bytes(2033, 1, 128, 16)
+    assert _noalloc(lib, B=2033, H=1, H_kv=1, d=128, S=16) == UNSUPPORTED
+    assert b"scratch" in lib.fa_last_error()
+    assert _noalloc(lib, B=32, H=32, H_kv=8, d=128, S=256) == UNSUPPORTED
+    # within the limit, a bad argument is still reported as such (no lookup, no launch)
+    assert _noalloc(lib, B=32, H=32, H_kv=8, d=128, S=16, lens=None) == INVALID

@@ -7,7 +7,8 @@ or a call fails, an exception is raised.
 
 Entry points mirror the C names: ``fwd`` (fa_fwd, bf16; with ``window=W``
 fa_fwd_window), ``fwd_f32`` (fa_fwd_f32), ``decode`` (fa_decode; with
-``window=W`` fa_decode_window), ``decode_paged`` (fa_decode_paged),
+``window=W`` fa_decode_window), ``decode_noalloc`` (fa_decode_noalloc),
+``decode_paged`` (fa_decode_paged),
 ``decode_fp8`` (fa_decode_fp8), ``decode_workspace_bytes``.
 ``scale=None`` means 1/sqrt(d), like the ``softmax_scale=None`` default of the
 flash_attn_func usage shown in "Attention mechanism evolution: MHA -> MLA,
@@ -23,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK, FA_ERR_INVALID_ARGUMENT, FA_ERR_UNSUPPORTED, FA_ERR_HIP = 0, 1, 2, 3
 
-EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode",
+EXPORTED = ("fa_fwd", "fa_fwd_window", "fa_fwd_f32", "fa_decode", "fa_decode_noalloc",
             "fa_decode_window", "fa_decode_paged", "fa_decode_fp8", "fa_decode_workspace_bytes",
             "fa_status_string", "fa_last_error")
 
@@ -57,6 +58,8 @@ def load():
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp, sz, vp]
     lib.fa_decode.restype = i
+    lib.fa_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.fa_decode_noalloc.restype = i
     lib.fa_decode_window.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, vp, sz, vp]
     lib.fa_decode_window.restype = i
     lib.fa_decode_paged.argtypes = [vp, vp, vp, vp, i, vp, vp, vp, i, i, i, i, i, i, f, i, vp, sz, vp]
@@ -168,11 +171,11 @@ def _decode_outputs(q, num_splits, out, lse, workspace):
     kernels write B*H rows of d values and B*H lse values)."""
     torch = _torch()
     B, H, d = q.shape
-    need = decode_workspace_bytes(B, H, d, num_splits)
     if workspace is None:
         # need == 0 means the arguments are invalid: the library call reports why
+        need = decode_workspace_bytes(B, H, d, num_splits)
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    else:
+    elif workspace is not False:           # False: the entry point needs none
         _require(workspace, "workspace", torch.uint8, 1, q.device)
     if out is None:
         out = torch.empty_like(q)
@@ -219,6 +222,31 @@ def decode(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | N
                                           seq_lens.data_ptr(), out.data_ptr(), _ptr(lse_t), B, H, H_kv, N_max, d,
                                           float(scale), int(window), int(num_splits), workspace.data_ptr(),
                                           workspace.numel(), _stream(q.device)))
+    return out, lse_t
+
+
+def decode_noalloc(q, k_cache, v_cache, seq_lens, num_splits: int = 16, scale: float | None = None,
+                   out=None, lse=None):
+    """fa_decode_noalloc: fa_decode with its split partials in the library's
+    per-GPU scratch array (no workspace; the library allocates nothing).  Calls
+    that overlap on one GPU race on that array.  ``out`` and ``lse`` are
+    allocated here when not given; pass them to allocate nothing at all."""
+    torch = _torch()
+    _require(q, "q", torch.bfloat16, 3)
+    _require(k_cache, "k_cache", torch.bfloat16, 4, q.device)
+    _require(v_cache, "v_cache", torch.bfloat16, 4, q.device)
+    _require(seq_lens, "seq_lens", torch.int32, 1, q.device)
+    B, H, d = q.shape
+    Bk, H_kv, N_max, dk = k_cache.shape
+    if Bk != B or dk != d or tuple(v_cache.shape) != tuple(k_cache.shape) or seq_lens.shape[0] != B:
+        raise ValueError("shape mismatch between q, caches and seq_lens")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _, out, lse_t = _decode_outputs(q, num_splits, out, lse, workspace=False)
+    with torch.cuda.device(q.device):
+        check(load().fa_decode_noalloc(q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(), seq_lens.data_ptr(),
+                                       out.data_ptr(), _ptr(lse_t), B, H, H_kv, N_max, d, float(scale),
+                                       int(num_splits), _stream(q.device)))
     return out, lse_t
 
 

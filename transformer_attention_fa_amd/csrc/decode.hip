@@ -37,6 +37,7 @@
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <cstdint>
 
 typedef int fa_dec_i32x4 __attribute__((ext_vector_type(4)));
@@ -677,6 +678,34 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
 }
 
 }  // namespace
+
+// Split partials of fa_decode_noalloc: a file-scope device array, so that
+// entry point needs no caller workspace and allocates nothing.  Each GPU the
+// library runs on holds its own copy until the process ends.  In host code the
+// name `scratch` is a host-side stand-in, not a device address: host code uses
+// only the per-device address decode_scratch() looks up.
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+hipError_t decode_scratch(void** ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* a = nullptr;
+        e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));   // with device `dev` current
+        if (e != hipSuccess) return e;
+        if (!a) return hipErrorInvalidSymbol;
+        addr[dev] = a;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream)
 {

@@ -99,7 +99,8 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
                           int num_splits, void* workspace, size_t workspace_bytes, int window,
                           hipStream_t stream, const char* name,
                           const int* block_table = nullptr, int max_blocks = 0, int page_size = 0,
-                          int num_pages = 0, int kv_fp8 = 0, float k_scale = 1.f, float v_scale = 1.f)
+                          int num_pages = 0, int kv_fp8 = 0, float k_scale = 1.f, float v_scale = 1.f,
+                          bool use_scratch = false)
 {
     fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
     if (s != FA_OK) return s;
@@ -121,9 +122,21 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
         return fail(FA_ERR_INVALID_ARGUMENT, "seq_lens must be 4-byte aligned");
     if (num_splits < 1 || num_splits > 256)
         return fail(FA_ERR_INVALID_ARGUMENT, "num_splits=%d outside 1..256", num_splits);
+    size_t need = workspace_bytes_for(B, H, d, num_splits);
+    if (use_scratch) {
+        // the library's scratch array instead of a caller workspace: checked
+        // against its size, and its address looked up only once every
+        // argument has passed
+        if (need == 0 || need > fa::kDecodeScratchBytes)
+            return fail(FA_ERR_UNSUPPORTED, "%s: B*H*num_splits*(d+1)*4 = %zu bytes of partials exceed the "
+                        "library's %zu-byte scratch array (fa_decode takes a caller workspace)", name, need,
+                        fa::kDecodeScratchBytes);
+        s = from_hip(fa::decode_scratch(&workspace), "scratch lookup");
+        if (s != FA_OK) return s;
+        workspace_bytes = fa::kDecodeScratchBytes;
+    }
     if (!workspace || !aligned(workspace, 16))
         return fail(FA_ERR_INVALID_ARGUMENT, "workspace must be non-null and 16-byte aligned");
-    size_t need = workspace_bytes_for(B, H, d, num_splits);
     if (need == 0 || workspace_bytes < need)
         return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
                     workspace_bytes, need);
@@ -220,6 +233,15 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
 {
     return decode_common(q, k_cache, v_cache, seq_lens, o, lse, B, H, H_kv, N_max, d, scale, num_splits,
                          workspace, workspace_bytes, 0, stream, "fa_decode");
+}
+
+fa_status_t fa_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                              const int* seq_lens, void* o, float* lse,
+                              int B, int H, int H_kv, int N_max, int d, float scale,
+                              int num_splits, hipStream_t stream)
+{
+    return decode_common(q, k_cache, v_cache, seq_lens, o, lse, B, H, H_kv, N_max, d, scale, num_splits, nullptr,
+                         0, 0, stream, "fa_decode_noalloc", nullptr, 0, 0, 0, 0, 1.f, 1.f, true);
 }
 
 fa_status_t fa_decode_window(const void* q, const void* k_cache, const void* v_cache,

@@ -55,6 +55,14 @@ struct DecodeArgs {
     float k_scale = 1.f, v_scale = 1.f;
 };
 
+// Size of the decode scratch array the allocation-free decode entry point
+// uses for its split partials (one array per GPU, in decode.hip).
+constexpr size_t kDecodeScratchBytes = size_t(16) << 20;
+
+// Device address of that array on the current device: looked up once per
+// device (hipGetSymbolAddress with the device current) and kept.
+hipError_t decode_scratch(void** ptr);
+
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
