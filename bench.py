@@ -19,9 +19,13 @@ Beside it, each timed the same way (back to back, its own roofline):
     a decode step, the step of the earlier benchmark;
   * ``next``: sliding-window and chunked prefill, windowed, paged and FP8 decode.
 
-Clock: right after every timed launch (outside its events) a probe kernel
-samples the shader clock on each XCD; each row reports the observed clock and
-its fraction of the matrix-core peak at that clock beside the 2.4 GHz one.
+Clock: after a prefill row is timed, the same launches run again, back to back,
+through the library's test hook fa_testing_fwd_capped with a clock record: the
+kernel's first workgroup on each XCD reads the shader-cycle counter
+(s_memtime) and the 100 MHz real-time counter (s_memrealtime) as it starts and
+as it finishes.  Each row reports that clock (the one the kernel ran at) and
+its fraction of the matrix-core peak at that clock beside the 2.4 GHz one, with
+the stamped launches' own times.
 
 CPU baseline: the fp64 oracle on one of the headline's four sequences, timed
 on the host cores and compared element by element with the GPU output.
@@ -44,8 +48,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s (% bf16 MFMA peak); decode KV GB/s (% HBM peak)"
 PEAK_CLOCK_GHZ = 2.4
-PROBE_TICKS = 300            # 3 us of the 100 MHz counter per probe
-PROBE_WORKGROUPS = 8         # one per XCD (workgroups go to the XCDs round robin)
 
 
 def log(msg):
@@ -160,77 +162,70 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
-class ClockProbe:
-    """Shader-clock samples taken right after timed launches (libfa_clock.so:
-    one single-wave workgroup per XCD reads the shader-cycle and 100 MHz
-    counters over PROBE_TICKS ticks)."""
+class ClockRecord:
+    """Clock records of prefill launches through the test hook
+    fa_testing_fwd_capped (csrc/fa_testing.h): per launch, 8 workgroups (one
+    per XCD) x {cycles at start, ticks at start, XCC id, cycles at end, ticks
+    at end} of the shader-cycle and 100 MHz counters."""
 
     def __init__(self, device, capacity):
         import torch
-        from transformer_attention_fa_amd import build
-        self.lib = ctypes.CDLL(build.PROBE_LIB)
-        self.lib.fa_clock_probe.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
-        self.lib.fa_clock_probe.restype = ctypes.c_int
-        self.buf = torch.zeros((capacity, PROBE_WORKGROUPS, 4), dtype=torch.int64, device=device)
+        from transformer_attention_fa_amd import api
+        self.lib = api.load()
+        fn = self.lib.fa_testing_fwd_capped
+        vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp]
+        fn.restype = i
+        self.buf = torch.zeros((capacity, 64), dtype=torch.int64, device=device)
         self.device = device
-        self.n = 0
 
-    def reset(self):
-        self.n = 0
-
-    def sample(self):
+    def launch(self, run, slot):
+        """One launch of run's problem with its clock record in buf[slot]."""
         import torch
-        if self.n >= self.buf.shape[0]:
-            return
-        st = self.lib.fa_clock_probe(self.buf[self.n].data_ptr(), PROBE_WORKGROUPS, PROBE_TICKS,
-                                     torch.cuda.current_stream(self.device).cuda_stream)
-        if st != 0:
-            raise RuntimeError(f"fa_clock_probe failed ({st})")
-        self.n += 1
+        from transformer_attention_fa_amd import api
+        s = run.spec
+        B, H, N_q, d = run.q.shape
+        api.check(self.lib.fa_testing_fwd_capped(
+            run.q.data_ptr(), run.k.data_ptr(), run.v.data_ptr(), run.o.data_ptr(), run.lse.data_ptr(), B, H,
+            run.k.shape[1], N_q, run.k.shape[2], d, float(s.scale), int(bool(s.causal)), int(s.window or 0), 0,
+            self.buf[slot].data_ptr(), torch.cuda.current_stream(self.device).cuda_stream))
 
-    def summary(self):
-        """Clock over the samples since reset (call after a synchronize)."""
+    def summary(self, n):
+        """Clock over the first n records (after a synchronize)."""
         import numpy as np
-        if self.n == 0:
-            return None
-        rec = self.buf[:self.n].cpu().numpy()
-        cyc, ticks, xcc = rec[..., 0].astype(np.float64), rec[..., 1].astype(np.float64), rec[..., 2]
-        per_sample = cyc.sum(axis=1) / ticks.sum(axis=1) * 0.1           # GHz (100 MHz ticks)
-        per_xcd = {}
-        for x in sorted(set(int(v) for v in xcc.ravel())):
-            m = xcc == x
-            per_xcd[str(x)] = round(float(np.median(cyc[m] / ticks[m] * 0.1)), 4)
-        return {"ghz_median": round(float(np.median(per_sample)), 4), "ghz_min": round(float(per_sample.min()), 4),
-                "ghz_max": round(float(per_sample.max()), 4), "ghz_median_per_xcd": per_xcd, "samples": self.n,
-                "method": f"s_memtime / s_memrealtime over {PROBE_TICKS} ticks of 100 MHz, one wave per XCD, "
-                          "right after each timed launch"}
+        rec = self.buf[:n].cpu().numpy().reshape(n, 8, 8)
+        cyc = (rec[..., 3] - rec[..., 0]).astype(np.float64)
+        ticks = (rec[..., 4] - rec[..., 1]).astype(np.float64)
+        xcc = rec[..., 2]
+        ghz = cyc / np.maximum(ticks, 1) * 0.1                      # per launch and workgroup
+        per_launch = np.median(ghz, axis=1)
+        per_xcd = {str(int(x)): round(float(np.median(ghz[xcc == x])), 4) for x in sorted(set(xcc.ravel().tolist()))}
+        return {"ghz_median": round(float(np.median(per_launch)), 4), "ghz_min": round(float(per_launch.min()), 4),
+                "ghz_max": round(float(per_launch.max()), 4), "ghz_median_per_xcd": per_xcd, "launches": n,
+                "workgroup_span_us_median": round(float(np.median(ticks)) / 100.0, 2),
+                "method": "inside the kernel: s_memtime (shader cycles) over s_memrealtime (100 MHz) from the "
+                          "start to the end of the first workgroup on each XCD, through fa_testing_fwd_capped"}
 
 
-def time_launches(fn, steps, warmup, probe=None):
+def time_launches(fn, steps, warmup):
     """Per-launch times (ms) of `steps` launches back to back, each bracketed by
-    HIP events on the current stream, a clock probe after each (outside the
-    events).  Returns (times, wall seconds of the timed loop, clock summary)."""
+    HIP events on the current stream; fn(i) makes launch i (i < 0: warm-up).
+    Returns (times, wall seconds of the timed loop)."""
     import numpy as np
     import torch
-    for _ in range(warmup):
-        fn()
-        if probe is not None:
-            probe.sample()
+    for i in range(warmup):
+        fn(-1 - i)
     torch.cuda.synchronize()
-    if probe is not None:
-        probe.reset()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
-    for a, b in ev:
+    for i, (a, b) in enumerate(ev):
         a.record()
-        fn()
+        fn(i)
         b.record()
-        if probe is not None:
-            probe.sample()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     t = np.array([a.elapsed_time(b) for a, b in ev])
-    return t, wall, (probe.summary() if probe is not None else None)
+    return t, wall
 
 
 def stats(t):
@@ -253,15 +248,12 @@ def mfma_roofline(tflops, key, clock):
     return r
 
 
-def hbm_roofline(gbps, key, clock=None):
+def hbm_roofline(gbps, key):
     from transformer_attention_fa_amd import roofline
-    r = {"bound": "hbm", "achieved": gbps, "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
-         "frac": gbps / roofline.PEAK_HBM_GBPS, "traffic": traffic_for(f"decode:{key}", ["decode.hip"]),
-         "kernel": "decode_split_kernel + decode_combine_kernel",
-         "counters": counters_for(f"decode:{key}", ["decode.hip"])}
-    if clock:
-        r["clock"] = clock
-    return r
+    return {"bound": "hbm", "achieved": gbps, "peak": roofline.PEAK_HBM_GBPS, "unit": "GB/s",
+            "frac": gbps / roofline.PEAK_HBM_GBPS, "traffic": traffic_for(f"decode:{key}", ["decode.hip"]),
+            "kernel": "decode_split_kernel + decode_combine_kernel",
+            "counters": counters_for(f"decode:{key}", ["decode.hip"])}
 
 
 def dev_bf16(bits, dev):
@@ -293,11 +285,13 @@ class PrefillRun:
         del self.q, self.k, self.v
 
 
-def prefill_row(run, steps, warmup, probe):
-    """One prefill workload timed back to back: TFLOP/s and its roofline."""
+def prefill_row(run, steps, warmup, clock):
+    """One prefill workload timed back to back through fa_fwd: TFLOP/s and its
+    roofline; then the same launches with a clock record (the clock the kernel
+    ran at, beside those launches' own times)."""
     spec = run.spec
     log(f"timing {spec.name}")
-    t, wall, clock = time_launches(run, steps, warmup, probe)
+    t, wall = time_launches(lambda i: run(), steps, warmup)
     st = stats(t)
     flops = spec.flops()
     tflops = flops / (st["ms_avg"] * 1e-3) / 1e12
@@ -308,7 +302,14 @@ def prefill_row(run, steps, warmup, probe):
            "exp_per_launch": flops / (4 * spec.d),
            "shape": {"B": spec.B, "H": spec.H, "H_kv": spec.H_kv, "N_q": spec.N_q, "N_k": spec.N_k, "d": spec.d,
                      "causal": spec.causal, "window": spec.window, "k_scale": spec.k_scale, "seed": spec.seed}}
-    row["roofline"] = mfma_roofline(tflops, spec.name, clock)
+    summary = None
+    if clock is not None and spec.d == 128:
+        n = min(steps, clock.buf.shape[0])
+        ts, _ = time_launches(lambda i: clock.launch(run, max(i, 0)), n, warmup)
+        summary = clock.summary(n)
+        summary["stamped_launch_ms_avg"] = float(ts.mean())
+        summary["stamped_tflops"] = flops / (ts.mean() * 1e-3) / 1e12
+    row["roofline"] = mfma_roofline(tflops, spec.name, summary)
     return row
 
 
@@ -338,11 +339,11 @@ class DecodeRun:
                    lse=self.lse, workspace=self.ws)
 
 
-def decode_row(run, steps, warmup, probe=None):
+def decode_row(run, steps, warmup):
     from transformer_attention_fa_amd import roofline
     spec = run.spec
     log(f"timing {spec.name}")
-    t, wall, clock = time_launches(run, steps, warmup, probe)
+    t, wall = time_launches(lambda i: run(), steps, warmup)
     st = stats(t)
     kv = roofline.decode_kv_bytes(spec.H_kv, spec.d, run.seq_lens)
     gbps = kv / (st["ms_avg"] * 1e-3) / 1e9
@@ -350,45 +351,50 @@ def decode_row(run, steps, warmup, probe=None):
             "wall_ms_per_launch": wall / steps * 1e3, "kv_bytes": kv,
             "shape": {"B": spec.B, "H": spec.H, "H_kv": spec.H_kv, "d": spec.d,
                       "seq_len_range": [spec.len_lo, spec.len_hi], "num_splits": spec.num_splits, "seed": spec.seed},
-            "roofline": hbm_roofline(gbps, spec.name, clock)}
+            "roofline": hbm_roofline(gbps, spec.name)}
 
 
-def interleaved_step(prun, drun, steps, warmup, probe):
+def interleaved_step(prun, drun, steps, warmup, clock):
     """Secondary figure: each MHA prefill launch alternates with a decode step
-    (prefill and decode timed by their own events; the probe follows the
-    prefill launch)."""
+    (each timed by its own events); then the same with the prefill launches
+    carrying a clock record."""
     import numpy as np
     import torch
     from transformer_attention_fa_amd import roofline
     log("timing the interleaved prefill + decode step")
-    for _ in range(warmup):
-        prun()
-        drun()
-    torch.cuda.synchronize()
-    probe.reset()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-    for e in ev:
-        e[0].record()
-        prun()
-        e[1].record()
-        probe.sample()
-        e[2].record()
-        drun()
-        e[3].record()
-    torch.cuda.synchronize()
-    tp = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    td = np.array([e[2].elapsed_time(e[3]) for e in ev])
+
+    def loop(launch, n):
+        for i in range(warmup):
+            launch(-1 - i)
+            drun()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        for i, e in enumerate(ev):
+            e[0].record()
+            launch(i)
+            e[1].record()
+            e[2].record()
+            drun()
+            e[3].record()
+        torch.cuda.synchronize()
+        return (np.array([e[0].elapsed_time(e[1]) for e in ev]), np.array([e[2].elapsed_time(e[3]) for e in ev]))
+
+    tp, td = loop(lambda i: prun(), steps)
+    n = min(steps, clock.buf.shape[0])
+    tps, _ = loop(lambda i: clock.launch(prun, max(i, 0)), n)
+    summary = clock.summary(n)
+    summary["stamped_launch_ms_avg"] = float(tps.mean())
     tf = prun.spec.flops() / (tp.mean() * 1e-3) / 1e12
     kv = roofline.decode_kv_bytes(drun.spec.H_kv, drun.spec.d, drun.seq_lens)
     return {"note": "secondary: each prefill launch alternates with a decode step; the memory-bound decode lets "
                     "the clock recover between prefill launches",
             "prefill": {"workload": prun.spec.name, "value": tf, "unit": "TFLOP/s", **stats(tp),
-                        "frac": tf / roofline.PEAK_BF16_TFLOPS, "clock": probe.summary()},
+                        "frac": tf / roofline.PEAK_BF16_TFLOPS, "clock": summary},
             "decode": {"workload": drun.spec.name, "value": kv / (td.mean() * 1e-3) / 1e9, "unit": "GB/s",
                        **stats(td)}}
 
 
-def measure_next(dev, steps, warmup, probe, drun=None):
+def measure_next(dev, steps, warmup, clock, drun=None):
     """The sliding-window, chunked-prefill, windowed, paged and FP8 decode rows,
     each on its own workload, back to back."""
     import numpy as np
@@ -397,7 +403,7 @@ def measure_next(dev, steps, warmup, probe, drun=None):
     out = {}
     for spec in (inputs.SWA_PREFILL, inputs.CHUNKED_PREFILL):
         run = PrefillRun(spec, dev)
-        out[spec.name] = prefill_row(run, steps, warmup, probe)
+        out[spec.name] = prefill_row(run, steps, warmup, clock)
         del run
     if drun is None:
         return out
@@ -407,7 +413,7 @@ def measure_next(dev, steps, warmup, probe, drun=None):
 
     def dec_row(entry, fn, kv, spec, **extra):
         log(f"timing {spec.name}")
-        t, wall, _ = time_launches(fn, steps, warmup)
+        t, wall = time_launches(lambda i: fn(), steps, warmup)
         st = stats(t)
         gbps = kv / (st["ms_avg"] * 1e-3) / 1e9
         return {"entry": entry, "value": gbps, "unit": "GB/s", "timing": "back to back", **st, "kv_bytes": kv,
@@ -491,7 +497,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": args.warmup + args.steps}))
         return
-    probe = ClockProbe(dev, max(args.steps, args.warmup))
+    clock = ClockRecord(dev, args.steps)
     base = {"metric": METRIC, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "higher_is_better": True,
             "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1), bf16)"}
     props = torch.cuda.get_device_properties(dev)
@@ -499,54 +505,54 @@ def main():
 
     if args.only == "prefill":
         spec = {"mha": inputs.MHA_PREFILL, "gqa": inputs.GQA_PREFILL, "mqa": inputs.MQA_PREFILL}[args.workload]
-        row = prefill_row(PrefillRun(spec, dev), args.steps, args.warmup, probe)
+        row = prefill_row(PrefillRun(spec, dev), args.steps, args.warmup, clock)
         print(json.dumps({**base, "value": row["value"], "unit": "TFLOP/s", "ms_per_step": row["wall_ms_per_launch"],
                           "config": {"workload": spec.name, **row["shape"], "timing": "back to back"},
                           "roofline": row["roofline"], "prefill": {spec.name: row}, "device": device}), flush=True)
         return
     if args.only == "decode":
-        row = decode_row(DecodeRun(inputs.GQA_DECODE, dev), args.steps, args.warmup, probe)
+        row = decode_row(DecodeRun(inputs.GQA_DECODE, dev), args.steps, args.warmup)
         print(json.dumps({**base, "value": row["value"], "unit": "GB/s", "ms_per_step": row["wall_ms_per_launch"],
                           "config": {"workload": inputs.GQA_DECODE.name, **row["shape"]}, "roofline": row["roofline"],
                           "decode": row, "device": device}), flush=True)
         return
     if args.only == "step":
         rec = interleaved_step(PrefillRun(inputs.MHA_PREFILL, dev), DecodeRun(inputs.GQA_DECODE, dev), args.steps,
-                               args.warmup, probe)
+                               args.warmup, clock)
         print(json.dumps({**base, "value": rec["prefill"]["value"], "unit": "TFLOP/s",
                           "config": {"workload": inputs.MHA_PREFILL.name + " + " + inputs.GQA_DECODE.name},
                           "interleaved_step": rec, "device": device}), flush=True)
         return
     if args.only == "next":
-        nxt = measure_next(dev, args.steps, args.warmup, probe, DecodeRun(inputs.GQA_DECODE, dev))
+        nxt = measure_next(dev, args.steps, args.warmup, clock, DecodeRun(inputs.GQA_DECODE, dev))
         print(json.dumps({**base, "next": nxt, "device": device}), flush=True)
         return
 
     # ---- the default run
     head_spec = inputs.MQA_PREFILL
     head = PrefillRun(head_spec, dev)
-    head_row = prefill_row(head, args.steps, args.warmup, probe)
+    head_row = prefill_row(head, args.steps, args.warmup, clock)
     head.free_inputs()
     rows = {head_spec.name: head_row}
     for spec in (inputs.GQA_PREFILL, inputs.MHA_PREFILL):
         run = PrefillRun(spec, dev)
-        rows[spec.name] = prefill_row(run, args.steps, args.warmup, probe)
+        rows[spec.name] = prefill_row(run, args.steps, args.warmup, clock)
         if spec is inputs.MHA_PREFILL:
             mha = run
         else:
             del run
     drun = DecodeRun(inputs.GQA_DECODE, dev)
-    drow = decode_row(drun, args.steps, args.warmup, probe)
+    drow = decode_row(drun, args.steps, args.warmup)
     rec = {**base, "value": head_row["value"], "unit": "TFLOP/s", "ms_per_step": head_row["wall_ms_per_launch"],
            "config": {"workload": head_spec.name, **head_row["shape"], "timing": "back to back"},
            "roofline": {**head_row["roofline"], "launch_ms_avg": head_row["ms_avg"],
                         "launch_ms_median": head_row["ms_median"], "launch_ms_min": head_row["ms_min"],
                         "flop_per_launch": head_row["flop_per_launch"], "exp_per_launch": head_row["exp_per_launch"]},
            "prefill": rows, "decode": drow,
-           "interleaved_step": interleaved_step(mha, drun, args.steps, args.warmup, probe)}
+           "interleaved_step": interleaved_step(mha, drun, args.steps, args.warmup, clock)}
     del mha
     if not args.no_next:
-        rec["next"] = measure_next(dev, args.steps, args.warmup, probe, drun)
+        rec["next"] = measure_next(dev, args.steps, args.warmup, clock, drun)
     del drun
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(head_spec, 1, head.o, head.lse)

@@ -75,13 +75,13 @@ def fwd_capped(q, k, v, causal, scale, max_workgroups, window=None):
     lib = api.load()
     fn = lib.fa_testing_fwd_capped
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+    fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp]
     fn.restype = i
     B, H, N_q, d = q.shape
     _, H_kv, N_k, _ = k.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
     api.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv, N_q, N_k, d,
-                 float(scale), int(bool(causal)), int(window or 0), int(max_workgroups),
+                 float(scale), int(bool(causal)), int(window or 0), int(max_workgroups), None,
                  torch.cuda.current_stream(q.device).cuda_stream))
     return o, lse

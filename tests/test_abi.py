@@ -202,10 +202,10 @@ def test_no_process_wide_settings_exported(lib):
 def _capped(lib, a, window, cap):
     fn = lib.fa_testing_fwd_capped
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
-    fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp]
+    fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp]
     fn.restype = i
     return fn(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["H_kv"], a["N_q"], a["N_k"], a["d"],
-              a["scale"], a["causal"], window, cap, None)
+              a["scale"], a["causal"], window, cap, None, None)
 
 
 @pytest.mark.parametrize("name,change,expect", FWD_CASES, ids=[c[0] for c in FWD_CASES])

@@ -648,6 +648,38 @@ def test_decode_fp8_workload_full_compare():
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
 
 
+def test_fwd_clock_record_hook():
+    """The test hook's clock-recording instantiation gives fa_fwd's bits, and
+    its records are plausible: XCC ids 0-7, end after start, and a shader
+    clock between 0.3 and 3 GHz."""
+    import ctypes
+    import torch
+    spec = _spec(2, 8, 2, 1000, 1000, 128, True, seed=97)
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    o_ref, l_ref = api.fwd(q, k, v, causal=True, scale=spec.scale)
+    lib = api.load()
+    fn = lib.fa_testing_fwd_capped
+    vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp]
+    fn.restype = i
+    stamps = torch.zeros(64, dtype=torch.int64, device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty_like(l_ref)
+    api.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), 2, 8, 2, 1000, 1000, 128,
+                 float(spec.scale), 1, 0, 0, stamps.data_ptr(), torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)) and torch.equal(lse, l_ref)
+    rec = stamps.cpu().numpy().reshape(8, 8)
+    assert ((rec[:, 2] >= 0) & (rec[:, 2] < 8)).all()
+    say(f"  XCC ids of workgroups 0-7: {rec[:, 2].tolist()}")
+    cyc, ticks = rec[:, 3] - rec[:, 0], rec[:, 4] - rec[:, 1]
+    assert (ticks > 0).all() and (cyc > 0).all()
+    ghz = cyc / ticks * 0.1
+    say(f"  clock record: {np.round(ghz, 3).tolist()} GHz")
+    assert ((ghz > 0.3) & (ghz < 3.0)).all()
+
+
 # ------------------------------------------------------------------ scale = 0
 @pytest.mark.parametrize("causal,window,d", [(True, None, 128), (False, None, 128), (True, 50, 128), (True, None, 64)])
 def test_fwd_scale_zero(causal, window, d):

@@ -23,11 +23,6 @@ ARCH = "gfx950"
 
 SOURCES = ["fa_api.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip"]
 
-# The benchmark's clock probe: its own small library, outside the attention
-# library and its ABI.
-PROBE_SOURCE = "clock_probe.hip"
-PROBE_LIB = os.path.join(PKG, "libfa_clock.so")
-
 COMMON_FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
@@ -58,27 +53,20 @@ def _compile(src: str, obj: str) -> None:
         raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}\n{res.stderr}")
 
 
-def _link(objs, lib: str) -> None:
-    out = lib + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(out, lib)
-
-
 def build(verbose: bool = False) -> str:
-    """Compile every source, link libfa.so and the probe library; returns the
-    path of libfa.so."""
+    """Compile every source and link libfa.so; returns its path."""
     with tempfile.TemporaryDirectory(prefix="fa_build_") as tmp:
-        srcs = SOURCES + [PROBE_SOURCE]
-        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in srcs]
-        with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-            list(ex.map(_compile, srcs, objs))
-        _link(objs[:len(SOURCES)], LIB)
-        _link(objs[len(SOURCES):], PROBE_LIB)
+        objs = [os.path.join(tmp, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+        with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+            list(ex.map(_compile, SOURCES, objs))
+        out = LIB + ".tmp"
+        cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
+        os.replace(out, LIB)
     if verbose:
-        print(f"built {LIB} and {PROBE_LIB}")
+        print(f"built {LIB}")
     return LIB
 
 

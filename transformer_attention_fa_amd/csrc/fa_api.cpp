@@ -195,7 +195,8 @@ fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, 
 
 fa_status_t fa_testing_fwd_capped(const void* q, const void* k, const void* v, void* o, float* lse,
                                   int B, int H, int H_kv, int N_q, int N_k, int d, float scale, int causal,
-                                  int window, int max_workgroups, hipStream_t stream)
+                                  int window, int max_workgroups, unsigned long long* clock_stamps,
+                                  hipStream_t stream)
 {
     fa_status_t s = check_common(q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale);
     if (s == FA_OK) s = check_fwd_grid(B, H, N_q, fa::kFwdBf16Rows, "fa_testing_fwd_capped");
@@ -206,6 +207,9 @@ fa_status_t fa_testing_fwd_capped(const void* q, const void* k, const void* v, v
         return fail(FA_ERR_INVALID_ARGUMENT, "max_workgroups=%d must be >= 0", max_workgroups);
     fa::FwdArgs a{q, k, v, o, lse, B, H, H_kv, N_q, N_k, d, scale, causal != 0, window};
     a.max_workgroups = max_workgroups;
+    if (clock_stamps && !aligned(clock_stamps, 8))
+        return fail(FA_ERR_INVALID_ARGUMENT, "clock_stamps must be 8-byte aligned");
+    a.clock_stamps = clock_stamps;
     return from_hip(fa::launch_fwd_bf16(a, stream), "fa_testing_fwd_capped launch");
 }
 

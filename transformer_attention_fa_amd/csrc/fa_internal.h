@@ -30,6 +30,7 @@ struct FwdArgs {
     int causal;
     int window;          // sliding window in keys (causal only), 0 = none
     int max_workgroups = 0;   // cap on the persistent grid, 0 = none (a test hook)
+    unsigned long long* clock_stamps = nullptr;   // bf16 prefill clock record (a test hook)
 };
 
 // One decode step, as validated by fa_decode.

@@ -13,6 +13,15 @@
  *                  < 0: FA_ERR_INVALID_ARGUMENT.
  *   window         0 = no window (causal as given), >= 1 = sliding window
  *                  (causal must be non-zero); < 0: FA_ERR_INVALID_ARGUMENT.
+ *   clock_stamps   NULL, or 64 u64 of device memory (8-byte aligned) for a
+ *                  clock record at d = 128 (a separate instantiation of the
+ *                  kernel, the product one has no such code): workgroups 0-7 (one per
+ *                  XCD) write, at stamps[8 g + 0 .. 2], the shader-cycle
+ *                  counter (s_memtime), the 100 MHz real-time counter
+ *                  (s_memrealtime) and the XCC id as they start, and at
+ *                  stamps[8 g + 3 .. 4] the two counters as they finish.
+ *                  Shader cycles over ticks times 100 MHz is the clock the
+ *                  workgroup ran at.  At d = 64 nothing is written.
  * Other arguments, layouts and errors as fa_fwd.
  */
 #ifndef FA_TESTING_H
@@ -26,7 +35,8 @@ extern "C" {
 
 fa_status_t fa_testing_fwd_capped(const void* q, const void* k, const void* v, void* o, float* lse,
                                   int B, int H, int H_kv, int N_q, int N_k, int d, float scale, int causal,
-                                  int window, int max_workgroups, hipStream_t stream);
+                                  int window, int max_workgroups, unsigned long long* clock_stamps,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

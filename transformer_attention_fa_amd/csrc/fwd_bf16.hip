@@ -70,6 +70,7 @@
 
 #include <hip/hip_runtime.h>
 #include <atomic>
+#include <cstddef>
 #include <cstdint>
 #include <type_traits>
 
@@ -116,7 +117,32 @@ struct Params {
     int grid;     // workgroups of the persistent grid
     int xcd;      // 1: the item list and the grid split per XCD (both multiples of 8)
     float c;      // scale * log2(e), > 0
+    // optional clock record (test hook; nullptr otherwise): workgroups 0-7,
+    // one per XCD, write {shader cycles, 100 MHz ticks, XCC id} at their start
+    // and {shader cycles, ticks} at their end to stamps[8 * g .. 8 * g + 4]
+    unsigned long long* stamps;
 };
+
+// Clock record of workgroup g < 8: s_memtime counts shader cycles and
+// s_memrealtime the constant 100 MHz clock, so the two spans give the clock
+// the kernel ran at.  One lane stores; nothing is kept in registers between
+// the two records.
+__device__ __forceinline__ void clock_stamp(unsigned long long* stamps, bool at_end)
+{
+    if (!stamps || blockIdx.x >= 8) return;
+    const unsigned long long t = __builtin_amdgcn_s_memtime();
+    const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x != 0) return;
+    unsigned long long* rec = stamps + 8 * blockIdx.x;
+    if (at_end) {
+        rec[3] = t;
+        rec[4] = rt;
+    } else {
+        rec[0] = t;
+        rec[1] = rt;
+        rec[2] = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf;    // HW_REG_XCC_ID, bits 3:0
+    }
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -176,7 +202,7 @@ __device__ __forceinline__ void decompose(int id, const Params& p, bool causal, 
     b = bh / p.H;
 }
 
-template <int D, int NW, bool CAUSAL, bool PERSIST>
+template <int D, int NW, bool CAUSAL, bool PERSIST, bool STAMPS>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 {
     static_assert(NW == 8, "the two wave groups pair up on the four SIMDs");
@@ -644,6 +670,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     int r = 0;
     int id = item_id(0);
     if (id < 0) return;
+    if constexpr (STAMPS) clock_stamp(p.stamps, false);
     cur = item_at(id);
     sb = 0;
     // prologue: the first item's Q block and first K tile
@@ -754,6 +781,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         cur = nxt;
         ++r;
     }
+    if constexpr (STAMPS) {
+        // the record pointer is read again from the kernel arguments here
+        // rather than kept in registers through the item loop
+        const char* kernarg = (const char*)__builtin_amdgcn_kernarg_segment_ptr();
+        clock_stamp(*reinterpret_cast<unsigned long long* const volatile*>(kernarg + offsetof(Params, stamps)), true);
+    }
 }
 
 // Workgroups that fit on the current device at once: the grid of the
@@ -775,7 +808,7 @@ int resident_blocks(K kernel, int threads)
     return n;
 }
 
-template <int D, int NW, bool CAUSAL, bool PERSIST>
+template <int D, int NW, bool CAUSAL, bool PERSIST, bool STAMPS = false>
 hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
@@ -798,12 +831,13 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     // scale 0 runs as a tiny positive scale: every exp2 argument then rounds to
     // 0 exactly as with scale 0, and masked scores stay -inf instead of NaN
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
+    p.stamps = a.clock_stamps;
     const long long items = (long long)p.nqb * a.H * a.B;   // at most 2^31 - 1: checked on the host
     if (items == 0) return hipSuccess;
     long long grid = items;
     int xcd = 0;
     if (PERSIST) {
-        const int resident = resident_blocks(fwd_bf16_kernel<D, NW, CAUSAL, PERSIST>, NW * 64);
+        const int resident = resident_blocks(fwd_bf16_kernel<D, NW, CAUSAL, PERSIST, STAMPS>, NW * 64);
         if (resident <= 0) return hipErrorInvalidDevice;
         if (resident < grid) grid = resident;
         if (a.max_workgroups > 0 && a.max_workgroups < grid) grid = a.max_workgroups;
@@ -817,7 +851,7 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     p.xcd = xcd;
     p.items = (int)items;
     p.grid = (int)grid;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, PERSIST>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, PERSIST, STAMPS>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -833,6 +867,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream)
     // d = 128 runs persistent (one workgroup per CU, item switches hidden
     // behind the next item's loads); d = 64 fits two workgroups per CU, which
     // hide each other's start and end, and runs one item per workgroup
+    if (a.d == 128 && a.clock_stamps)   // the test hook's clock record: its own instantiation
+        return a.causal ? launch<128, 8, true, true, true>(a, group, stream)
+                        : launch<128, 8, false, true, true>(a, group, stream);
     if (a.d == 128)
         return a.causal ? launch<128, 8, true, true>(a, group, stream) : launch<128, 8, false, true>(a, group, stream);
     if (a.d == 64)
