@@ -3,7 +3,9 @@
 
 Every figure is timed on inputs resident in HBM with preallocated outputs;
 each launch is bracketed by HIP events recorded on the stream it runs on (the
-current stream, which the binding passes to the library).
+current stream, which the binding passes to the library).  Each timed loop
+follows a warm-up of at least --warmup launches and 0.25 s of back-to-back
+launches, so the device clock has settled under the load.
 
 Headline (``value``, ``roofline``): fa_fwd on the largest prefill workload,
 MQA B=4, H=64, H_kv=1, N=4096, d=128, non-causal, bf16 -- one step is one
@@ -207,14 +209,26 @@ class ClockRecord:
                           "start to the end of the first workgroup on each XCD, through fa_testing_fwd_capped"}
 
 
+WARMUP_SECONDS = 0.25
+
+
 def time_launches(fn, steps, warmup):
     """Per-launch times (ms) of `steps` launches back to back, each bracketed by
     HIP events on the current stream; fn(i) makes launch i (i < 0: warm-up).
-    Returns (times, wall seconds of the timed loop)."""
+    Warm-up: `warmup` launches, continued until WARMUP_SECONDS of back-to-back
+    launches have run -- after the host-side input drawing the device idles
+    for seconds, and its clock takes tens of milliseconds of load to settle
+    (ten launches of a 0.3 ms kernel measured 10 % slower than the same
+    launches right after).  Returns (times, wall seconds of the timed loop)."""
     import numpy as np
     import torch
-    for i in range(warmup):
+    t_start = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_start < WARMUP_SECONDS:
         fn(-1 - i)
+        i += 1
+        if i % max(warmup, 1) == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
@@ -364,9 +378,14 @@ def interleaved_step(prun, drun, steps, warmup, clock):
     log("timing the interleaved prefill + decode step")
 
     def loop(launch, n):
-        for i in range(warmup):
+        t_start = time.perf_counter()
+        i = 0
+        while i < warmup or time.perf_counter() - t_start < WARMUP_SECONDS:
             launch(-1 - i)
             drun()
+            i += 1
+            if i % max(warmup, 1) == 0:
+                torch.cuda.synchronize()
         torch.cuda.synchronize()
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
         for i, e in enumerate(ev):
