@@ -445,8 +445,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             if constexpr (NL > 0) cur = nxt;
         });
     };
-    // vector phase: mask, online softmax and P for tile j (held in s)
-    auto softmax_phase = [&](int j) __attribute__((always_inline)) {
+    // vector phase: mask, online softmax and P for tile j (held in s).
+    // NOMASK: the tile is known to be whole for every row of the wave.
+    auto softmax_phase = [&](int j, auto nomaskc) __attribute__((always_inline)) {
+        constexpr bool NOMASK = decltype(nomaskc)::value;
         const int key0 = j * BN;
         const bool need_mask = (key0 + BN > p.N_k) || (CAUSAL && key0 + BN - 1 > qw0 + off);
         // Element masks.  Lane (l32, half) holds keys kt*32 + 8*(r/4) + r%4 +
@@ -466,7 +468,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         auto low_bits = [](int n) __attribute__((always_inline)) {
             return n >= 32 ? 0xffffffffu : n <= 0 ? 0u : (1u << n) - 1u;
         };
-        if (need_mask) {
+        if (!NOMASK && need_mask) {
             const int lim = last_vis - key0 - 4 * half;
             const int vis_lo = (CAUSAL ? min(qw0 + off, p.N_k - 1) : p.N_k - 1) - key0;   // over the wave's rows
             const int vis_hi = (CAUSAL ? min(qw0 + 31 + off, p.N_k - 1) : p.N_k - 1) - key0;
@@ -482,7 +484,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             }
         }
         // keys before the window of some row of this wave
-        if (windowed && key0 < qw0 + 31 + off - p.window + 1) {
+        if (!NOMASK && windowed && key0 < qw0 + 31 + off - p.window + 1) {
             const int lo = first_vis - key0 - 4 * half;
             const int win_lo = qw0 + off - p.window + 1 - key0;      // over the wave's rows
             const int win_hi = qw0 + 31 + off - p.window + 1 - key0;
@@ -577,25 +579,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     // slots, and saying so keeps the compiler from waiting for the loads
     // before the first read (their order across periods comes from the
     // explicit wait and the barrier).
-    auto period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, char* __restrict__ kdst,
+    auto period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, auto steadyc, char* __restrict__ kdst,
                       char* __restrict__ vdst, const char* __restrict__ kt, const char* __restrict__ vt)
                       __attribute__((always_inline)) {
         constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value, SM = decltype(smc)::value;
         constexpr int ROLE = decltype(rolec)::value;     // 0, 1, or 2 = either (no matrix-core phase)
+        // STEADY: K tile j+1 and V tile j belong to this item and K tile j+1
+        // is whole, no Q slice of the next item loads in this period, and the
+        // tile the softmax works on needs no mask
+        constexpr bool STEADY = decltype(steadyc)::value;
         // this wave's loads of the previous period landed (the item's first
         // period follows the item switch, which waited already)
-        if (j != cur.kb_lo) __builtin_amdgcn_s_waitcnt(0x0f70);
+        if (STEADY || j != cur.kb_lo) __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
         // K tile j+1 (or the next item's first) and V tile j.  Waves 0-3 load
         // them, one load after every other MFMA of their matrix-core phase:
         // those waves wait for the matrix core there anyway, while eight waves
         // issuing 32 loads at the barrier stall on the shared issue queue.
         // Without a matrix-core phase in this period they load at once.
-        const bool ldk = j + 1 < cur.nkb || (has_next && j == j_knext);
-        const bool ldv = j < cur.nkb;
-        const i32x4 rk = j + 1 < cur.nkb ? tile_rsrc(kbase, j + 1)
+        const bool ldk = STEADY || j + 1 < cur.nkb || (has_next && j == j_knext);
+        const bool ldv = STEADY || j < cur.nkb;
+        const i32x4 rk = STEADY ? make_rsrc(kbase + (size_t)(j + 1) * TILE, TILE)
+                       : j + 1 < cur.nkb ? tile_rsrc(kbase, j + 1)
                                          : tile_rsrc(reinterpret_cast<const char*>(p.k + (size_t)nxt.bg * (size_t)p.N_k * D), nxt.kb_lo);
-        const i32x4 rv = tile_rsrc(vbase, j);
+        const i32x4 rv = STEADY ? make_rsrc(vbase + (size_t)j * TILE, TILE) : tile_rsrc(vbase, j);
         auto spread = [&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i % 2 == 0 && i / 2 < LOADS0) {
@@ -619,13 +626,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         // smallest power of two that fits them in (1 for items of QPARTS
         // tiles or more: a short item does not load it all in one burst).  An
         // item without key tiles has one period, which loads it all.
-        if (has_next) {
+        if (!STEADY && has_next) {
             const int part_lo = min(QPARTS, (j - cur.kb_lo) * qpp);
             const int part_hi = min(QPARTS, (j - cur.kb_lo + 1) * qpp);
             for (int part = part_lo; part < part_hi; ++part) issue_q(nxt, part);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (SM == 1) softmax_phase(j - 1);
+        if constexpr (SM == 1) softmax_phase(j - 1, steadyc);
         if constexpr (FIRST < LAST) {
             __builtin_amdgcn_s_setprio(1);           // matrix-core phase first when both waves are ready
             if constexpr (ROLE == 0) run_steps(firstc, lastc, kt, vt, spread);
@@ -633,13 +640,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
-        if constexpr (SM == 2) softmax_phase(j);
+        if constexpr (SM == 2) softmax_phase(j, steadyc);
     };
     // slots of period j: K tile j+1 and V tile j load, K tile j and V tile j-1
     // are read
-    auto run_period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec) __attribute__((always_inline)) {
+    auto run_period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, auto steadyc) __attribute__((always_inline)) {
         const int b = (j + sb) & 1;
-        period(j, firstc, lastc, smc, rolec, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE, lds + b * TILE,
+        period(j, firstc, lastc, smc, rolec, steadyc, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE, lds + b * TILE,
                lds + (2 + (b ^ 1)) * TILE);
     };
     using C0 = std::integral_constant<int, 0>;
@@ -647,6 +654,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     using C2 = std::integral_constant<int, 2>;
     using CNPV = std::integral_constant<int, NPV>;
     using CNSTEP = std::integral_constant<int, NSTEP>;
+    using CF = std::false_type;       // a general period
+    using CT = std::true_type;        // a steady period
 
 
     // ---- the workgroup's items: round r of a persistent grid of p.grid
@@ -698,20 +707,48 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         l_b = 0.f;
 
         int j = cur.kb_lo;
-        for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{}, C2{});    // tiles before this wave's window
+        for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{}, C2{}, CF{});    // tiles before this wave's window
         if (nkb_w > a_w) {
+            // Steady periods (see period()) j, lo <= j < hi:
+            //  * after the first period and the periods that load the next
+            //    item's Q slices;
+            //  * K tile j+1 and V tile j whole (j + 1 < full, the whole tiles)
+            //    and of this item (j + 1 < nkb, so not the next item's first
+            //    K tile either);
+            //  * the tile the softmax works on (j for waves 0-3, j-1 for
+            //    waves 4-7) whole for every row of the wave: t_lo <= t < t_hi,
+            //    where t_hi is the first tile reaching past N_k or past the
+            //    wave's first row's last visible key, and t_lo (window) the
+            //    first tile inside the window of the wave's last row;
+            //  * within the wave's matrix-core periods (j < nkb_w).
+            const int qperiods = has_next ? (QPARTS + qpp - 1) / qpp : 0;
+            const int full = p.N_k / BN;
+            int t_hi = full;
+            if (CAUSAL) t_hi = min(t_hi, max(0, qw0 + off + 1) / BN);
+            int t_lo = 0;
+            if (windowed) t_lo = max(0, qw0 + 31 + off - p.window + 1 + BN - 1) / BN;
+            const int s_lo = cur.kb_lo + max(1, qperiods);
+            const int s_hi = min(min(nkb_w, cur.nkb - 1), full - 1);
             if (role == 0) {
-                run_period(j, CNPV{}, CNSTEP{}, C2{}, C0{});
-                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{});
-                run_period(j, C0{}, CNPV{}, C0{}, C0{});            // j == nkb_w: PV of the last tile
+                run_period(j, CNPV{}, CNSTEP{}, C2{}, C0{}, CF{});
+                const int lo = min(max(j + 1, max(s_lo, t_lo)), nkb_w);       // softmax of tile j
+                const int hi = max(lo, min(s_hi, t_hi));
+                for (++j; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
+                for (; j < hi; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CT{});
+                for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
+                run_period(j, C0{}, CNPV{}, C0{}, C0{}, CF{});            // j == nkb_w: PV of the last tile
             } else {
-                run_period(j, CNPV{}, CNSTEP{}, C0{}, C1{});
-                for (++j; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{});
-                run_period(j, C0{}, CNPV{}, C1{}, C1{});
+                run_period(j, CNPV{}, CNSTEP{}, C0{}, C1{}, CF{});
+                const int lo = min(max(j + 1, max(s_lo, t_lo + 1)), nkb_w);   // softmax of tile j-1
+                const int hi = max(lo, min(s_hi, t_hi + 1));
+                for (++j; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
+                for (; j < hi; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CT{});
+                for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
+                run_period(j, C0{}, CNPV{}, C1{}, C1{}, CF{});
             }
             ++j;
         }
-        for (; j <= cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{}, C2{});  // tiles after this wave's rows
+        for (; j <= cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{}, C2{}, CF{});  // tiles after this wave's rows
 
         // ---- item switch.  Epilogue: O = O_acc / l (bf16), lse = ln2 * (m +
         //      log2 l).  A lane holds 4-element pieces of one row, so storing
