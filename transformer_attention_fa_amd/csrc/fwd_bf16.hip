@@ -313,6 +313,8 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 
     Item cur, nxt;
     bool has_next;
+    i32x4 rq_nxt;            // the next item's Q block (descriptor), for the steady periods' Q slices
+    int q_lim;               // steady periods j < q_lim load Q slice j - kb_lo of the next item
     int sb;                  // slot parity: tile t of the current item lives in slot (t + sb) % 2
     int j_knext;             // period that loads the next item's first K tile
     int qpp;                 // parts of the next item's Q block loaded per period
@@ -579,9 +581,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     // slots, and saying so keeps the compiler from waiting for the loads
     // before the first read (their order across periods comes from the
     // explicit wait and the barrier).
-    auto period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, auto steadyc, char* __restrict__ kdst,
-                      char* __restrict__ vdst, const char* __restrict__ kt, const char* __restrict__ vt)
-                      __attribute__((always_inline)) {
+    auto period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, auto steadyc, const i32x4& rk_in,
+                      const i32x4& rv_in, char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ kt,
+                      const char* __restrict__ vt) __attribute__((always_inline)) {
         constexpr int FIRST = decltype(firstc)::value, LAST = decltype(lastc)::value, SM = decltype(smc)::value;
         constexpr int ROLE = decltype(rolec)::value;     // 0, 1, or 2 = either (no matrix-core phase)
         // STEADY: K tile j+1 and V tile j belong to this item and K tile j+1
@@ -599,10 +601,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         // Without a matrix-core phase in this period they load at once.
         const bool ldk = STEADY || j + 1 < cur.nkb || (has_next && j == j_knext);
         const bool ldv = STEADY || j < cur.nkb;
-        const i32x4 rk = STEADY ? make_rsrc(kbase + (size_t)(j + 1) * TILE, TILE)
+        const i32x4 rk = STEADY ? rk_in
                        : j + 1 < cur.nkb ? tile_rsrc(kbase, j + 1)
                                          : tile_rsrc(reinterpret_cast<const char*>(p.k + (size_t)nxt.bg * (size_t)p.N_k * D), nxt.kb_lo);
-        const i32x4 rv = STEADY ? make_rsrc(vbase + (size_t)j * TILE, TILE) : tile_rsrc(vbase, j);
+        const i32x4 rv = STEADY ? rv_in : tile_rsrc(vbase, j);
         auto spread = [&](auto ic) __attribute__((always_inline)) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i % 2 == 0 && i / 2 < LOADS0) {
@@ -631,6 +633,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             const int part_hi = min(QPARTS, (j - cur.kb_lo + 1) * qpp);
             for (int part = part_lo; part < part_hi; ++part) issue_q(nxt, part);
         }
+        if (STEADY && j < q_lim) {
+            // one slice a period (items of QPARTS tiles or more), its
+            // descriptor made once per item
+            const int part = j - cur.kb_lo;
+            fa_raw_buffer_load_lds(rq_nxt, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
+                                   ld_voff + part * NTHR * 16, 0, 0, kStreamOnce);
+        }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SM == 1) softmax_phase(j - 1, steadyc);
         if constexpr (FIRST < LAST) {
@@ -644,10 +653,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     };
     // slots of period j: K tile j+1 and V tile j load, K tile j and V tile j-1
     // are read
-    auto run_period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, auto steadyc) __attribute__((always_inline)) {
+    auto run_period = [&](int j, auto firstc, auto lastc, auto smc, auto rolec, auto steadyc,
+                          const i32x4& rk_in = i32x4{}, const i32x4& rv_in = i32x4{}) __attribute__((always_inline)) {
         const int b = (j + sb) & 1;
-        period(j, firstc, lastc, smc, rolec, steadyc, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE, lds + b * TILE,
-               lds + (2 + (b ^ 1)) * TILE);
+        period(j, firstc, lastc, smc, rolec, steadyc, rk_in, rv_in, lds + (b ^ 1) * TILE, lds + (2 + b) * TILE,
+               lds + b * TILE, lds + (2 + (b ^ 1)) * TILE);
+    };
+    // steady periods j .. hi-1 with the tile descriptors carried from period
+    // to period (advanced by a tile, a 48-bit add), not rebuilt
+    auto advance = [](i32x4 r) __attribute__((always_inline)) {
+        const uint64_t a = ((uint64_t)(uint32_t)r[1] << 32 | (uint32_t)r[0]) + (uint64_t)TILE;
+        r[0] = (int)(uint32_t)a;
+        r[1] = (int)(uint32_t)(a >> 32);
+        return r;
+    };
+    auto run_steady = [&](int& j, int hi, auto smc, auto rolec) __attribute__((always_inline)) {
+        if (j >= hi) return;
+        i32x4 rk = make_rsrc(kbase + (size_t)(j + 1) * TILE, TILE);
+        i32x4 rv = make_rsrc(vbase + (size_t)j * TILE, TILE);
+        for (; j < hi; ++j) {
+            run_period(j, std::integral_constant<int, 0>{}, std::integral_constant<int, NSTEP>{}, smc, rolec,
+                       std::true_type{}, rk, rv);
+            rk = advance(rk);
+            rv = advance(rv);
+        }
     };
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
@@ -655,7 +684,6 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     using CNPV = std::integral_constant<int, NPV>;
     using CNSTEP = std::integral_constant<int, NSTEP>;
     using CF = std::false_type;       // a general period
-    using CT = std::true_type;        // a steady period
 
 
     // ---- the workgroup's items: round r of a persistent grid of p.grid
@@ -698,6 +726,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         j_knext = max(cur.kb_lo, cur.nkb - 1);
         qpp = 1;
         while (qpp < QPARTS && qpp * (cur.nkb - cur.kb_lo) < QPARTS) qpp *= 2;
+        q_lim = has_next && qpp == 1 ? cur.kb_lo + QPARTS : cur.kb_lo;
+        if (has_next)
+            rq_nxt = make_rsrc(p.q + ((size_t)nxt.bh * (size_t)p.N_q + (size_t)nxt.q0) * D,
+                               (unsigned)max(0, min(BM, p.N_q - nxt.q0)) * ROWB);
         set_wave();
 #pragma unroll
         for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
@@ -711,7 +743,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         if (nkb_w > a_w) {
             // Steady periods (see period()) j, lo <= j < hi:
             //  * after the first period and the periods that load the next
-            //    item's Q slices;
+            //    item's Q slices (unless they load one slice each);
             //  * K tile j+1 and V tile j whole (j + 1 < full, the whole tiles)
             //    and of this item (j + 1 < nkb, so not the next item's first
             //    K tile either);
@@ -727,14 +759,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             if (CAUSAL) t_hi = min(t_hi, max(0, qw0 + off + 1) / BN);
             int t_lo = 0;
             if (windowed) t_lo = max(0, qw0 + 31 + off - p.window + 1 + BN - 1) / BN;
-            const int s_lo = cur.kb_lo + max(1, qperiods);
+            const int s_lo = cur.kb_lo + max(1, qpp == 1 ? 0 : qperiods);
             const int s_hi = min(min(nkb_w, cur.nkb - 1), full - 1);
             if (role == 0) {
                 run_period(j, CNPV{}, CNSTEP{}, C2{}, C0{}, CF{});
                 const int lo = min(max(j + 1, max(s_lo, t_lo)), nkb_w);       // softmax of tile j
                 const int hi = max(lo, min(s_hi, t_hi));
                 for (++j; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
-                for (; j < hi; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CT{});
+                run_steady(j, hi, C2{}, C0{});
                 for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
                 run_period(j, C0{}, CNPV{}, C0{}, C0{}, CF{});            // j == nkb_w: PV of the last tile
             } else {
@@ -742,7 +774,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 const int lo = min(max(j + 1, max(s_lo, t_lo + 1)), nkb_w);   // softmax of tile j-1
                 const int hi = max(lo, min(s_hi, t_hi + 1));
                 for (++j; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
-                for (; j < hi; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CT{});
+                run_steady(j, hi, C1{}, C1{});
                 for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
                 run_period(j, C0{}, CNPV{}, C1{}, C1{}, CF{});
             }
