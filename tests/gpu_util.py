@@ -65,14 +65,14 @@ def compare(o_gpu, lse_gpu, o_ref, lse_ref, o_tol, lse_tol, lse_relative=True, l
     return do, dl
 
 
-def fwd_capped(q, k, v, causal, scale, max_workgroups, window=None):
+def fwd_capped(q, k, v, causal, scale, max_workgroups, window=None, lib=None):
     """The bf16 prefill with a cap on its persistent grid, through the library's
     test hook fa_testing_fwd_capped (a per-call cap; results do not depend on
-    it).  Returns (o, lse)."""
+    it), on libfa.so or the library handle `lib`.  Returns (o, lse)."""
     import ctypes
     import torch
     from transformer_attention_fa_amd import api
-    lib = api.load()
+    lib = lib or api.load()
     fn = lib.fa_testing_fwd_capped
     vp, i, f = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
     fn.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, i, i, vp, vp]
@@ -81,7 +81,8 @@ def fwd_capped(q, k, v, causal, scale, max_workgroups, window=None):
     _, H_kv, N_k, _ = k.shape
     o = torch.empty_like(q)
     lse = torch.empty((B, H, N_q), dtype=torch.float32, device=q.device)
-    api.check(fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv, N_q, N_k, d,
-                 float(scale), int(bool(causal)), int(window or 0), int(max_workgroups), None,
-                 torch.cuda.current_stream(q.device).cuda_stream))
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), B, H, H_kv, N_q, N_k, d,
+            float(scale), int(bool(causal)), int(window or 0), int(max_workgroups), None,
+            torch.cuda.current_stream(q.device).cuda_stream)
+    assert st == api.FA_OK, (st, lib.fa_last_error().decode())
     return o, lse

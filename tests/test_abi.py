@@ -146,6 +146,30 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
         api.load()
 
 
+@pytest.fixture(scope="module")
+def debug_lib_path():
+    from transformer_attention_fa_amd import build
+    if not os.path.exists(build.DEBUG_LIB):
+        build.build(debug_barriers=True)
+    return build.DEBUG_LIB
+
+
+def test_debug_barrier_build_exports_the_same_boundary(debug_lib_path):
+    dbg = api.open_library(debug_lib_path)
+    for name in declared_functions() + ["fa_testing_fwd_capped"]:
+        assert hasattr(dbg, name), name
+        assert ctypes.cast(getattr(dbg, name), ctypes.c_void_p).value
+
+
+def test_fa_library_selects_another_build(monkeypatch, debug_lib_path):
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.setenv("FA_LIBRARY", debug_lib_path)
+    assert api.load()._name == debug_lib_path
+    monkeypatch.setattr(api, "_lib", None)
+    monkeypatch.delenv("FA_LIBRARY")
+    assert api.load()._name == api.LIB_PATH
+
+
 GOOD_PAGED = dict(q=P, kp=P, vp=P, bt=P, max_blocks=8, lens=P, o=P, lse=P, B=4, H=8, H_kv=2, num_pages=64,
                   page_size=32, d=128, scale=0.1, S=16, ws=P, ws_bytes=1 << 20)
 

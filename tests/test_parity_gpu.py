@@ -4,6 +4,8 @@ Every comparison covers the whole output, element by element: small problems
 that span several query and key tiles and end in ragged tails, and the
 full-size workloads in the launch configuration the benchmark times.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -869,3 +871,36 @@ def test_concurrent_streams_match_sequential():
         assert torch.equal(o1, o_a) and torch.equal(l1, l_a)
         assert torch.equal(o2, o_b) and torch.equal(l2, l_b)
         assert torch.equal(do1, do_a) and torch.equal(dl1, dl_a)
+
+
+# ------------------------------------------------------------------ race hunting
+DEBUG_BARRIER_CASES = [
+    # B, H, H_kv, N_q, N_k, d, causal, window, cap
+    (2, 8, 2, 600, 600, 128, True, None, 3),
+    (1, 8, 1, 900, 900, 128, False, None, 5),
+    (1, 8, 2, 900, 900, 128, True, 70, 8),
+    (1, 8, 1, 900, 300, 128, True, None, 2),
+    (2, 4, 4, 300, 1000, 128, True, None, 0),
+    (1, 4, 2, 517, 517, 64, True, None, 0),
+]
+
+
+@pytest.mark.parametrize("case", DEBUG_BARRIER_CASES, ids=lambda c: "x".join(str(x) for x in c))
+def test_fwd_debug_barrier_build_is_bit_identical(case):
+    """libfa_debug_barriers.so puts a full wait and a barrier between the two
+    phases of every period; the arithmetic is the same, so any difference from
+    libfa.so would come from a race between waves."""
+    import torch
+    from transformer_attention_fa_amd import build
+    B, H, H_kv, N_q, N_k, d, causal, window, cap = case
+    if not os.path.exists(build.DEBUG_LIB):
+        pytest.fail(f"{build.DEBUG_LIB} is not built (python -m transformer_attention_fa_amd.build --debug-barriers)")
+    dbg = api.open_library(build.DEBUG_LIB)
+    spec = _spec(B, H, H_kv, N_q, N_k, d, causal, seed=53)
+    say(f"debug-barrier build vs libfa.so: {spec.name} window={window} cap={cap}")
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    o, lse = fwd_capped(q, k, v, causal, spec.scale, cap, window)
+    o2, lse2 = fwd_capped(q, k, v, causal, spec.scale, cap, window, lib=dbg)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)

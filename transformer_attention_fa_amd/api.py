@@ -37,16 +37,14 @@ class FAError(RuntimeError):
         self.status = status
 
 
-def load():
-    """Open libfa.so (built in-tree) and declare the C signatures."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
+def open_library(path: str):
+    """Open a build of the library at `path` (its own handle) and declare the C
+    signatures."""
+    if not os.path.exists(path):
         raise FileNotFoundError(
-            f"{LIB_PATH} is not built; run `python -m transformer_attention_fa_amd.build` "
+            f"{path} is not built; run `python -m transformer_attention_fa_amd.build` "
             "(there is no fallback path)")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, i, vp]
     lib.fa_fwd.restype = i
@@ -70,8 +68,16 @@ def load():
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
-    _lib = lib
     return lib
+
+
+def load():
+    """Open libfa.so (built in-tree; FA_LIBRARY names another build, such as
+    the race-hunting libfa_debug_barriers.so) once per process."""
+    global _lib
+    if _lib is None:
+        _lib = open_library(os.environ.get("FA_LIBRARY") or LIB_PATH)
+    return _lib
 
 
 def check(status: int) -> None:

@@ -123,6 +123,20 @@ struct Params {
     unsigned long long* stamps;
 };
 
+// Race-hunting build (-DFA_DEBUG_BARRIERS): one more barrier in the middle
+// of every period, between the two phases of each wave, after every memory
+// operation of the wave has completed.  Every wave passes it once per period,
+// whatever its role, so the barrier counts stay equal; the arithmetic is
+// unchanged, so the output must be bit-identical to the normal build's.
+__device__ __forceinline__ void debug_barrier()
+{
+#ifdef FA_DEBUG_BARRIERS
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#endif
+}
+
 // Clock record of workgroup g < 8: s_memtime counts shader cycles and
 // s_memrealtime the constant 100 MHz clock, so the two spans give the clock
 // the kernel ran at.  One lane stores; nothing is kept in registers between
@@ -642,6 +656,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SM == 1) softmax_phase(j - 1, steadyc);
+        if constexpr (ROLE != 0) debug_barrier();
         if constexpr (FIRST < LAST) {
             __builtin_amdgcn_s_setprio(1);           // matrix-core phase first when both waves are ready
             if constexpr (ROLE == 0) run_steps(firstc, lastc, kt, vt, spread);
@@ -649,6 +664,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             __builtin_amdgcn_s_setprio(0);
             __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (ROLE == 0) debug_barrier();
         if constexpr (SM == 2) softmax_phase(j, steadyc);
     };
     // slots of period j: K tile j+1 and V tile j load, K tile j and V tile j-1
