@@ -264,7 +264,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     }
     auto issue = [&](const char* base, int kb, char* dst) __attribute__((always_inline)) {
         const int key0 = kb * BN;
-        const unsigned bytes = (unsigned)min(BN, p.N_k - key0) * ROWB;
+        const unsigned bytes = (unsigned)max(0, min(BN, p.N_k - key0)) * ROWB;
         const i32x4 rs = make_rsrc(base + (size_t)key0 * ROWB, bytes);
 #pragma unroll
         for (int i = 0; i < LOADS; ++i)
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     }
     auto tile_rsrc = [&](const char* base, int kb) __attribute__((always_inline)) {
         const int key0 = kb * BN;
-        return make_rsrc(base + (size_t)key0 * ROWB, (unsigned)min(BN, p.N_k - key0) * ROWB);
+        return make_rsrc(base + (size_t)key0 * ROWB, (unsigned)max(0, min(BN, p.N_k - key0)) * ROWB);
     };
     auto issue0 = [&](const i32x4& rs, char* dst, int i) __attribute__((always_inline)) {
         fa_raw_buffer_load_lds(rs, (LDS_AS void*)(dst + (i * (NTHR / 2) + (w & 3) * 64) * 16), 16,
@@ -313,6 +313,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         // keys ending at its last causally visible key) the block's first row
         // sees nothing before its window
         if (CAUSAL && p.window > 0) it.kb_lo = min(it.nkb, max(0, it.q0 + off - p.window + 1) / BN);
+        // at least two tiles (one for an item alone in its workgroup): the
+        // padding lies past N_k or past every row's causal limit, is loaded
+        // as zeros or as keys no row sees, and is masked
+        it.nkb = max(it.nkb, it.kb_lo + (PERSIST ? 2 : 1));
         return it;
     };
     // Q block of an item into the Q area (16-byte chunks swizzled like a K
@@ -332,6 +336,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     int sb;                  // slot parity: tile t of the current item lives in slot (t + sb) % 2
     int j_knext;             // period that loads the next item's first K tile
     int qpp;                 // parts of the next item's Q block loaded per period
+    int q_first;             // first period of the item that may load the next item's Q block
     const char* kbase;
     const char* vbase;
     int qw0, qi, last_vis, first_vis, nkb_w, a_w;
@@ -604,9 +609,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         // is whole, no Q slice of the next item loads in this period, and the
         // tile the softmax works on needs no mask
         constexpr bool STEADY = decltype(steadyc)::value;
-        // this wave's loads of the previous period landed (the item's first
-        // period follows the item switch, which waited already)
-        if (STEADY || j != cur.kb_lo) __builtin_amdgcn_s_waitcnt(0x0f70);
+        // this wave's loads of the previous period landed (waves 4-7 issued
+        // nothing but output stores in the switch period before the item's
+        // second period)
+        if (STEADY || !(role == 1 && j == q_first)) __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
         // K tile j+1 (or the next item's first) and V tile j.  Waves 0-3 load
         // them, one load after every other MFMA of their matrix-core phase:
@@ -637,20 +643,20 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                 if (ldv) issue0(rv, vdst, i);
             }
         }
-        // The next item's Q block: qpp parts per period over periods kb_lo ..
-        // nkb-1, so that it has landed when the last period starts; qpp is the
-        // smallest power of two that fits them in (1 for items of QPARTS
+        // The next item's Q block: qpp parts per period over periods q_first
+        // .. nkb-1, so that it has landed when the last period starts; qpp is
+        // the smallest power of two that fits them in (1 for items of QPARTS
         // tiles or more: a short item does not load it all in one burst).  An
-        // item without key tiles has one period, which loads it all.
+        // item with no period before its last loads it all in the last.
         if (!STEADY && has_next) {
-            const int part_lo = min(QPARTS, (j - cur.kb_lo) * qpp);
-            const int part_hi = min(QPARTS, (j - cur.kb_lo + 1) * qpp);
+            const int part_lo = min(QPARTS, (j - q_first) * qpp);
+            const int part_hi = min(QPARTS, (j - q_first + 1) * qpp);
             for (int part = part_lo; part < part_hi; ++part) issue_q(nxt, part);
         }
         if (STEADY && j < q_lim) {
             // one slice a period (items of QPARTS tiles or more), its
             // descriptor made once per item
-            const int part = j - cur.kb_lo;
+            const int part = j - q_first;
             fa_raw_buffer_load_lds(rq_nxt, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
                                    ld_voff + part * NTHR * 16, 0, 0, kStreamOnce);
         }
@@ -720,91 +726,18 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         return k < p.items ? k : -1;
     };
 
-    int r = 0;
-    int id = item_id(0);
-    if (id < 0) return;
-    if constexpr (STAMPS) clock_stamp(p.stamps, false);
-    cur = item_at(id);
-    sb = 0;
-    // prologue: the first item's Q block and first K tile
-#pragma unroll
-    for (int part = 0; part < QPARTS; ++part) issue_q(cur, part);
-    if (cur.nkb > cur.kb_lo)
-        issue(reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D), cur.kb_lo, lds + (cur.kb_lo & 1) * TILE);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
-    read_q();
-
-    for (;;) {
-        const int nid = item_id(r + 1);
-        has_next = PERSIST && nid >= 0;
-        nxt = has_next ? item_at(nid) : cur;
-        j_knext = max(cur.kb_lo, cur.nkb - 1);
-        qpp = 1;
-        while (qpp < QPARTS && qpp * (cur.nkb - cur.kb_lo) < QPARTS) qpp *= 2;
-        q_lim = has_next && qpp == 1 ? cur.kb_lo + QPARTS : cur.kb_lo;
-        if (has_next)
-            rq_nxt = make_rsrc(p.q + ((size_t)nxt.bh * (size_t)p.N_q + (size_t)nxt.q0) * D,
-                               (unsigned)max(0, min(BM, p.N_q - nxt.q0)) * ROWB);
-        set_wave();
-#pragma unroll
-        for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
-        m_run = kNegInf;
-        nbase = 0.f;
-        l_a = 0.f;
-        l_b = 0.f;
-
-        int j = cur.kb_lo;
-        for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{}, C2{}, CF{});    // tiles before this wave's window
-        if (nkb_w > a_w) {
-            // Steady periods (see period()) j, lo <= j < hi:
-            //  * after the first period and the periods that load the next
-            //    item's Q slices (unless they load one slice each);
-            //  * K tile j+1 and V tile j whole (j + 1 < full, the whole tiles)
-            //    and of this item (j + 1 < nkb, so not the next item's first
-            //    K tile either);
-            //  * the tile the softmax works on (j for waves 0-3, j-1 for
-            //    waves 4-7) whole for every row of the wave: t_lo <= t < t_hi,
-            //    where t_hi is the first tile reaching past N_k or past the
-            //    wave's first row's last visible key, and t_lo (window) the
-            //    first tile inside the window of the wave's last row;
-            //  * within the wave's matrix-core periods (j < nkb_w).
-            const int qperiods = has_next ? (QPARTS + qpp - 1) / qpp : 0;
-            const int full = p.N_k / BN;
-            int t_hi = full;
-            if (CAUSAL) t_hi = min(t_hi, max(0, qw0 + off + 1) / BN);
-            int t_lo = 0;
-            if (windowed) t_lo = max(0, qw0 + 31 + off - p.window + 1 + BN - 1) / BN;
-            const int s_lo = cur.kb_lo + max(1, qpp == 1 ? 0 : qperiods);
-            const int s_hi = min(min(nkb_w, cur.nkb - 1), full - 1);
-            if (role == 0) {
-                run_period(j, CNPV{}, CNSTEP{}, C2{}, C0{}, CF{});
-                const int lo = min(max(j + 1, max(s_lo, t_lo)), nkb_w);       // softmax of tile j
-                const int hi = max(lo, min(s_hi, t_hi));
-                for (++j; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
-                run_steady(j, hi, C2{}, C0{});
-                for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
-                run_period(j, C0{}, CNPV{}, C0{}, C0{}, CF{});            // j == nkb_w: PV of the last tile
-            } else {
-                run_period(j, CNPV{}, CNSTEP{}, C0{}, C1{}, CF{});
-                const int lo = min(max(j + 1, max(s_lo, t_lo + 1)), nkb_w);   // softmax of tile j-1
-                const int hi = max(lo, min(s_hi, t_hi + 1));
-                for (++j; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
-                run_steady(j, hi, C1{}, C1{});
-                for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
-                run_period(j, C0{}, CNPV{}, C1{}, C1{}, CF{});
-            }
-            ++j;
-        }
-        for (; j <= cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{}, C2{}, CF{});  // tiles after this wave's rows
-
-        // ---- item switch.  Epilogue: O = O_acc / l (bf16), lse = ln2 * (m +
-        //      log2 l).  A lane holds 4-element pieces of one row, so storing
-        //      straight from the accumulators would write 32 rows x 8 bytes per
-        //      instruction.  Each wave stages its 32 x D tile in LDS (16-byte
-        //      chunks XOR-swizzled by row) and reads it back row-major: every
-        //      global store is then 4 (or 8) whole rows, 1 KB contiguous, and
-        //      non-temporal (O is written once).
+    // ---- output of a finished item.  O = O_acc / l (bf16), lse = ln2 * (m +
+    //      log2 l).  A lane holds 4-element pieces of one row, so storing
+    //      straight from the accumulators would write 32 rows x 8 bytes per
+    //      instruction.  Each wave stages its 32 x D tile in LDS (16-byte
+    //      chunks XOR-swizzled by row) and reads it back row-major: every
+    //      global store is then 4 (or 8) whole rows, 1 KB contiguous, and
+    //      non-temporal (O is written once).
+    constexpr int RPI = 64 / CPR;                  // rows per wave-wide 16-byte read
+    u32x4 pend[32 / RPI];                          // this wave's output rows, row-major
+    // row sums, the LSE of rows qw0_ .. qw0_+31 of head bh, and the output
+    // rows staged at ow and read back into pend
+    auto finish = [&](char* ow, unsigned bh, int qw0_) __attribute__((always_inline)) {
         float l_tot;
         {
             const float l_run = l_a + l_b;
@@ -812,60 +745,236 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         }
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-        if (p.lse && half == 0 && qi < p.N_q)
-            p.lse[(size_t)cur.bh * (size_t)p.N_q + qi] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
-        constexpr int RPI = 64 / CPR;                  // rows per wave-wide 16-byte read
-        u32x4 pend[32 / RPI];                          // this wave's output rows, row-major
-        auto stage = [&](char* ow) __attribute__((always_inline)) {
+        if (p.lse && half == 0 && qw0_ + l32 < p.N_q)
+            p.lse[(size_t)bh * (size_t)p.N_q + qw0_ + l32] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : kNegInf;
 #pragma unroll
-            for (int dm = 0; dm < DBLK; ++dm)
+        for (int dm = 0; dm < DBLK; ++dm)
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq) {
-                    f32x4 t;
+            for (int gq = 0; gq < 4; ++gq) {
+                f32x4 t;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
-                    const int c = 4 * dm + gq;         // 16-byte chunk of the row (elements 8c .. 8c+7)
-                    *reinterpret_cast<bf16x4*>(ow + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
-                        __builtin_convertvector(t, bf16x4);
-                }
-#pragma unroll
-            for (int k = 0; k < 32 / RPI; ++k) {
-                const int rr = k * RPI + lane / CPR, c = lane % CPR;
-                pend[k] = *reinterpret_cast<const u32x4*>(ow + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
+                for (int i = 0; i < 4; ++i) t[i] = oacc[dm][gq * 4 + i] * inv;
+                const int c = 4 * dm + gq;         // 16-byte chunk of the row (elements 8c .. 8c+7)
+                *reinterpret_cast<bf16x4*>(ow + l32 * ROWB + ((c ^ (l32 & (CPR - 1))) * 16) + half * 8) =
+                    __builtin_convertvector(t, bf16x4);
             }
-        };
-        auto store_pend = [&]() __attribute__((always_inline)) {
 #pragma unroll
-            for (int k = 0; k < 32 / RPI; ++k) {
-                const int rr = k * RPI + lane / CPR, c = lane % CPR;
-                if (qw0 + rr < p.N_q)
-                    __builtin_nontemporal_store(pend[k], reinterpret_cast<u32x4*>(p.o + ((size_t)cur.bh * (size_t)p.N_q + qw0 + rr) * D + c * 8));
-            }
-        };
-        // The next item's Q block landed before the last period (see the
-        // period's loads), so every wave takes its next Q fragments now,
-        // stages its output in those same rows of the Q area, and holds the
-        // output in registers across the switch barrier: the stores issue
-        // after it, so the barrier's wait for the next item's loads does not
-        // also wait for them.  An item without key tiles loads the next Q
-        // block in its only period: it does all of that after the barrier.
-        const bool late_q = has_next && cur.nkb == cur.kb_lo;
-        if (!late_q) {
-            if (has_next) read_q();
-            stage(qw_lds);
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int rr = k * RPI + lane / CPR, c = lane % CPR;
+            pend[k] = *reinterpret_cast<const u32x4*>(ow + rr * ROWB + ((c ^ (rr & (CPR - 1))) * 16));
         }
+    };
+    auto store_pend = [&](unsigned bh, int qw0_) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < 32 / RPI; ++k) {
+            const int rr = k * RPI + lane / CPR, c = lane % CPR;
+            if (qw0_ + rr < p.N_q)
+                __builtin_nontemporal_store(pend[k], reinterpret_cast<u32x4*>(p.o + ((size_t)bh * (size_t)p.N_q + qw0_ + rr) * D + c * 8));
+        }
+    };
+    auto reset_rows = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < DBLK; ++i) oacc[i] = f32x16{};
+        m_run = kNegInf;
+        nbase = 0.f;
+        l_a = 0.f;
+        l_b = 0.f;
+    };
+
+    int r = 0;
+    int id = item_id(0);
+    if (id < 0) return;
+    if constexpr (STAMPS) clock_stamp(p.stamps, false);
+    cur = item_at(id);
+    sb = 0;
+    // the item after the current one (round r + 1)
+    auto look_ahead = [&]() __attribute__((always_inline)) {
+        const int nid = item_id(r + 1);
+        has_next = PERSIST && nid >= 0;
+        nxt = has_next ? item_at(nid) : cur;
+    };
+    look_ahead();
+
+    // ---- switch periods.  Period nkb of an item (PV of its last tile) and
+    //      period kb_lo of the next (S of its first tile) are one period, with
+    //      one barrier; the first item's first period and the last item's last
+    //      are such periods too, with no item before or after.  In it every
+    //      wave, for the item it leaves (if it computes that item's last tile):
+    //      softmax of that tile (waves 4-7), its PV product; then takes its Q
+    //      fragments of the item it enters, writes the finished rows out
+    //      (staged in its own rows of the Q area, which hold the entered
+    //      item's Q block until those fragments are read and the next Q block
+    //      only from the next period on), and, for the entered item (if it
+    //      computes that item's first tile): the S product, softmax (waves
+    //      0-3).  Waves 0-3 load the entered item's tiles of the period (K
+    //      tile kb_lo+1, V tile kb_lo) during its S product, or at once.
+    //      Between switch periods an item runs periods kb_lo+1 .. nkb-1; items
+    //      have at least two key tiles (padding tiles lie past N_k or past
+    //      every row's causal limit and are masked), so the next item's Q
+    //      block always has a period to load in.
+    // (the slot pointers are restrict-qualified parameters, as in period())
+    auto switch_body = [&](auto rolec, bool has_prev, bool has_cur, bool do_pv, int j_last, unsigned prev_bh,
+                           int prev_qw0, char* __restrict__ kdst, char* __restrict__ vdst, const char* __restrict__ kt,
+                           const char* __restrict__ vt) __attribute__((always_inline)) {
+        constexpr int RL = decltype(rolec)::value;
+        static_assert(2 * (2 * LOADS0) <= mma_index(NPV, NSTEP), "the tile loads fit in the S product");
         __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
-        if (late_q) {
-            read_q();
-            stage(qw_lds);
+        if constexpr (RL == 1) {
+            if (do_pv) softmax_phase(j_last, CF{});      // with the finished item's rows
         }
-        store_pend();
-        if (!has_next) break;
-        sb = (j_knext + 1 + sb - nxt.kb_lo) & 1;   // the next item's first K tile sits in slot (j_knext + 1 + sb) % 2
-        cur = nxt;
-        ++r;
-    }
+        __builtin_amdgcn_sched_barrier(0);
+        if (do_pv) {
+            __builtin_amdgcn_s_setprio(1);
+            run_steps(C0{}, CNPV{}, kt, vt, [](auto) {});
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (has_cur) {
+            set_wave();
+            read_q();
+        }
+        if (has_prev) {
+            finish(qw_lds, prev_bh, prev_qw0);
+            store_pend(prev_bh, prev_qw0);
+        }
+        reset_rows();
+        if (!has_cur) return;
+        const bool do_s = nkb_w > a_w && a_w == cur.kb_lo;
+        const int j = cur.kb_lo;
+        const bool ldk = j + 1 < cur.nkb || (has_next && j == j_knext);
+        const i32x4 rk = j + 1 < cur.nkb ? tile_rsrc(kbase, j + 1)
+                                        : tile_rsrc(reinterpret_cast<const char*>(p.k + (size_t)nxt.bg * (size_t)p.N_k * D), nxt.kb_lo);
+        const i32x4 rv = tile_rsrc(vbase, j);
+        auto spread = [&](auto ic) __attribute__((always_inline)) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i % 2 == 0 && i / 2 < LOADS0) {
+                if (ldk) issue0(rk, kdst, i / 2);
+            } else if constexpr (i % 2 == 0 && i / 2 < 2 * LOADS0) {
+                issue0(rv, vdst, i / 2 - LOADS0);
+            }
+        };
+        __builtin_amdgcn_sched_barrier(0);
+        if (do_s) {
+            __builtin_amdgcn_s_setprio(1);
+            if constexpr (RL == 0) run_steps(CNPV{}, CNSTEP{}, kt, vt, spread);
+            else run_steps(CNPV{}, CNSTEP{}, kt, vt, [](auto) {});
+            __builtin_amdgcn_s_setprio(0);
+            __builtin_amdgcn_sched_barrier(0);
+        } else if (RL == 0) {
+#pragma unroll
+            for (int i = 0; i < LOADS0; ++i) {
+                if (ldk) issue0(rk, kdst, i);
+                issue0(rv, vdst, i);
+            }
+        }
+        if constexpr (RL == 0) {
+            if (do_s) softmax_phase(j, CF{});
+        }
+    };
+    // the switch period; mb: the K slot of the entered item's first tile
+    auto switch_period = [&](auto rolec, bool has_prev, bool has_cur, bool do_pv, int j_last, unsigned prev_bh,
+                             int prev_qw0, int mb) __attribute__((always_inline)) {
+        switch_body(rolec, has_prev, has_cur, do_pv, j_last, prev_bh, prev_qw0, lds + (mb ^ 1) * TILE,
+                    lds + (2 + mb) * TILE, lds + mb * TILE, lds + (2 + (mb ^ 1)) * TILE);
+    };
+
+    // prologue: the first item's Q block and first K tile
+#pragma unroll
+    for (int part = 0; part < QPARTS; ++part) issue_q(cur, part);
+    issue(reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D), cur.kb_lo, lds + (cur.kb_lo & 1) * TILE);
+    __builtin_amdgcn_s_waitcnt(0x0f70);
+    __syncthreads();
+
+    // The item loop, compiled once per wave role (the two roles carry
+    // different registers from period to period)
+    auto item_loop = [&](auto rolec) __attribute__((always_inline)) {
+        constexpr int RL = decltype(rolec)::value;
+        bool has_prev = false, has_cur = true, do_pv = false;
+        int j_last = 0, prev_qw0 = 0;
+        unsigned prev_bh = 0;
+        int mb = cur.kb_lo & 1;                  // K slot of the entered item's first tile
+        j_knext = max(cur.kb_lo, cur.nkb - 1);
+        for (;;) {
+            switch_period(rolec, has_prev, has_cur, do_pv, j_last, prev_bh, prev_qw0, mb);
+            if (!has_cur) break;
+            // the next item's Q block loads in periods q_first .. nkb-1
+            q_first = cur.kb_lo + 1;
+            const int qcount = cur.nkb - q_first;
+            qpp = 1;
+            while (qpp < QPARTS && qpp * qcount < QPARTS) qpp *= 2;
+            q_lim = has_next && qpp == 1 ? q_first + QPARTS : q_first;
+            if (has_next)
+                rq_nxt = make_rsrc(p.q + ((size_t)nxt.bh * (size_t)p.N_q + (size_t)nxt.q0) * D,
+                                   (unsigned)max(0, min(BM, p.N_q - nxt.q0)) * ROWB);
+            // this wave's first period (S of tile a_w) ran in the switch period
+            // when the wave starts at the item's first tile; its last (PV of
+            // tile nkb-1) runs in the next one when it ends at the item's last
+            const bool started = a_w == cur.kb_lo;
+            const bool ends = nkb_w == cur.nkb;
+            int j = q_first;
+            for (; j < a_w; ++j) run_period(j, C0{}, C0{}, C0{}, C2{}, CF{});    // tiles before this wave's window
+            if (nkb_w > a_w) {
+                // Steady periods (see period()) j, lo <= j < hi:
+                //  * after the first period after the switch period and the
+                //    periods that load the next item's Q slices (unless they
+                //    load one slice each);
+                //  * K tile j+1 and V tile j whole (j + 1 < full, the whole
+                //    tiles) and of this item (j + 1 < nkb, so not the next
+                //    item's first K tile either);
+                //  * the tile the softmax works on (j for waves 0-3, j-1 for
+                //    waves 4-7) whole for every row of the wave: t_lo <= t <
+                //    t_hi, where t_hi is the first tile reaching past N_k or
+                //    past the wave's first row's last visible key, and t_lo
+                //    (window) the first tile inside the window of the wave's
+                //    last row;
+                //  * within the wave's matrix-core periods (j < nkb_w).
+                const int qperiods = has_next ? (QPARTS + qpp - 1) / qpp : 0;
+                const int full = p.N_k / BN;
+                int t_hi = full;
+                if (CAUSAL) t_hi = min(t_hi, max(0, qw0 + off + 1) / BN);
+                int t_lo = 0;
+                if (windowed) t_lo = max(0, qw0 + 31 + off - p.window + 1 + BN - 1) / BN;
+                const int s_lo = q_first + max(1, qpp == 1 ? 0 : qperiods);
+                const int s_hi = min(min(nkb_w, cur.nkb - 1), full - 1);
+                if constexpr (RL == 0) {
+                    if (!started) run_period(j++, CNPV{}, CNSTEP{}, C2{}, C0{}, CF{});
+                    const int lo = min(max(j, max(s_lo, t_lo)), nkb_w);           // softmax of tile j
+                    const int hi = max(lo, min(s_hi, t_hi));
+                    for (; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
+                    run_steady(j, hi, C2{}, C0{});
+                    for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C2{}, C0{}, CF{});
+                    if (!ends) run_period(j++, C0{}, CNPV{}, C0{}, C0{}, CF{});   // j == nkb_w: PV of the last tile
+                } else {
+                    if (!started) run_period(j++, CNPV{}, CNSTEP{}, C0{}, C1{}, CF{});
+                    const int lo = min(max(j, max(s_lo, t_lo + 1)), nkb_w);       // softmax of tile j-1
+                    const int hi = max(lo, min(s_hi, t_hi + 1));
+                    for (; j < lo; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
+                    run_steady(j, hi, C1{}, C1{});
+                    for (; j < nkb_w; ++j) run_period(j, C0{}, CNSTEP{}, C1{}, C1{}, CF{});
+                    if (!ends) run_period(j++, C0{}, CNPV{}, C1{}, C1{}, CF{});
+                }
+            }
+            for (; j < cur.nkb; ++j) run_period(j, C0{}, C0{}, C0{}, C2{}, CF{});  // tiles after this wave's rows
+            // the next switch period leaves this item
+            has_prev = true;
+            do_pv = nkb_w > a_w && nkb_w == cur.nkb;
+            j_last = cur.nkb - 1;
+            prev_bh = cur.bh;
+            prev_qw0 = qw0;
+            mb = (cur.nkb + sb) & 1;
+            has_cur = has_next;
+            if (has_next) {
+                sb = (j_knext + 1 + sb - nxt.kb_lo) & 1;   // the next item's first K tile sits in slot (j_knext + 1 + sb) % 2
+                cur = nxt;
+                ++r;
+                look_ahead();
+                j_knext = max(cur.kb_lo, cur.nkb - 1);
+            }
+        }
+    };
+    if (role == 0) item_loop(C0{});
+    else item_loop(C1{});
     if constexpr (STAMPS) {
         // the record pointer is read again from the kernel arguments here
         // rather than kept in registers through the item loop
