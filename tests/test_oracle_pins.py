@@ -224,19 +224,24 @@ def test_scale_is_applied_to_scores():
 # run by torch on the CPU in fp64, and torch's own scaled_dot_product_attention.
 # --------------------------------------------------------------------------
 def _torch_reference(q, k, v, scale, causal):
+    """fp64 torch: query heads grouped as [B, H_kv, rep, N_q, d] against their
+    shared K/V head by broadcasting (no copies of K/V), scores masked with
+    -inf, then log-sum-exp and the weights exp(s - lse) applied to V."""
     import torch
-    qt, kt, vt = (torch.from_numpy(np.ascontiguousarray(x)).double() for x in (q, k, v))
-    rep = qt.shape[1] // kt.shape[1]
-    kt = kt.repeat_interleave(rep, dim=1)
-    vt = vt.repeat_interleave(rep, dim=1)
-    s = torch.matmul(qt, kt.transpose(-2, -1).contiguous()) * scale
-    n_q, n_k = s.shape[-2:]
+    B, H, n_q, d = q.shape
+    H_kv, n_k = k.shape[1], k.shape[2]
+    qt = torch.from_numpy(np.ascontiguousarray(q)).double().reshape(B, H_kv, H // H_kv, n_q, d)
+    kt = torch.from_numpy(np.ascontiguousarray(k)).double().unsqueeze(2)        # [B, H_kv, 1, n_k, d]
+    vt = torch.from_numpy(np.ascontiguousarray(v)).double().unsqueeze(2)
+    s = (qt.unsqueeze(-2) * kt.unsqueeze(-3)).sum(-1) * scale                   # [B, H_kv, rep, n_q, n_k]
     if causal:
-        keep = torch.ones(n_q, n_k, dtype=torch.bool).tril(diagonal=n_k - n_q)
-        s = s.masked_fill(~keep, float("-inf"))
+        rows = torch.arange(n_q).reshape(n_q, 1)
+        cols = torch.arange(n_k).reshape(1, n_k)
+        s = s.masked_fill(cols > rows + (n_k - n_q), float("-inf"))
     lse = torch.logsumexp(s, dim=-1)
-    o = torch.matmul(torch.softmax(s, dim=-1), vt)
-    return o.numpy(), lse.numpy()
+    w = torch.exp(s - lse.unsqueeze(-1))
+    o = (w.unsqueeze(-1) * vt.unsqueeze(-4)).sum(-2)                            # [B, H_kv, rep, n_q, d]
+    return o.reshape(B, H, n_q, d).numpy(), lse.reshape(B, H, n_q).numpy()
 
 
 @pytest.mark.parametrize("shape", [(2, 4, 2, 33, 33, 16), (1, 8, 1, 17, 40, 8), (2, 6, 3, 40, 17, 12),
