@@ -14,7 +14,7 @@
 // f = 0, or f = max(0, len - W) with a sliding window of W keys ("Attention
 // variants" §4: the newest token sees the W most recent rows), and serves up to 16
 // query heads that share one KV head, so each K/V byte of the chunk crosses HBM
-// once for all of them.  The chunk is cut into 16-key tiles dealt round robin
+// once for all of them.  The chunk is cut into 16-key tiles (32 for FP8) dealt round robin
 // to the 4 waves; each wave streams its tiles into its own slice of LDS with
 // buffer_load_dwordx4 ... lds (two tiles in flight, no workgroup barrier) and
 // computes on the matrix cores:
@@ -24,6 +24,13 @@
 // In the 16x16 accumulator layout lane l holds head l%16 and keys 4*(l/16)..+3
 // of the tile, which is exactly the B operand the 16x16x16 P V product needs,
 // so P goes from the score registers to the matrix core with one conversion.
+// An FP8 E4M3 cache (1 byte a value) streams 32-key tiles, the same bytes per
+// tile: K codes are read 8 at a time and converted to bf16 in registers (exact)
+// for two 16-key S products; V^T comes from the FP8 tile itself through the
+// transposing 8-bit read ds_read_b64_tr_b8 (each lane gets one d column of 8
+// keys), converted in registers and multiplied with v_mfma_f32_16x16x32_bf16,
+// whose B operand -- 8 keys per lane -- is the lane's scores of both 16-key
+// blocks (the V rows are read in that key order).
 // Padding heads (past the group) have zero queries and are discarded.  The
 // online softmax of "Attention variants" §3 runs per wave (running max raised
 // only when a tile max exceeds it by more than 8, so p <= 256); the 4 waves
@@ -58,6 +65,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 #define LDS_AS __attribute__((address_space(3)))
 
@@ -134,6 +142,17 @@ __device__ __forceinline__ int fswz(int r, int c)
 {
     if constexpr (D == 128) return c ^ ((r >> 1) & 7);
     else return c ^ ((r >> 2) & 3);
+}
+
+// Position of 16-byte chunk c of row r (0..31) of a 32-key FP8 V tile.  The
+// transposing 8-bit reads of a d block take one chunk of 8 rows per 16 lanes
+// (rows 4g..4g+3 and 16+4g..16+4g+3 for lane group g); this layout spreads the
+// 16 rows of each half wave over all 64 banks.
+template <int D>
+__device__ __forceinline__ int vswz8(int r, int c)
+{
+    if constexpr (D == 128) return c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
+    else return c ^ (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
 }
 
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
@@ -260,6 +279,41 @@ __device__ __forceinline__ void lds_read_b64n(u32x2 (&a)[N], const unsigned (&p)
                      : "v"(p[0]), "v"(p[1])
                      : "memory");
 }
+// eight 8-byte LDS reads (the FP8 K fragments of a 32-key tile)
+__device__ __forceinline__ void lds_read_b64x8(u32x2 (&a)[8], const unsigned (&p)[8])
+{
+    asm volatile("ds_read_b64 %0, %8\n\tds_read_b64 %1, %9\n\tds_read_b64 %2, %10\n\tds_read_b64 %3, %11\n\t"
+                 "ds_read_b64 %4, %12\n\tds_read_b64 %5, %13\n\tds_read_b64 %6, %14\n\tds_read_b64 %7, %15\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]),
+                   "=&v"(a[7])
+                 : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+                 : "memory");
+}
+// transposing 8 x 8-bit reads: in each 16-lane group, lane 2k+h reads 8
+// bytes (row k, columns 8h..8h+7 of an 8 x 16 byte block) and lane i
+// receives column i of the 8 rows (byte k from row k)
+template <int N>
+__device__ __forceinline__ void lds_read_tr8(u32x2 (&a)[N], const unsigned (&p)[N])
+{
+    if constexpr (N == 8)
+        asm volatile("ds_read_b64_tr_b8 %0, %8\n\tds_read_b64_tr_b8 %1, %9\n\t"
+                     "ds_read_b64_tr_b8 %2, %10\n\tds_read_b64_tr_b8 %3, %11\n\t"
+                     "ds_read_b64_tr_b8 %4, %12\n\tds_read_b64_tr_b8 %5, %13\n\t"
+                     "ds_read_b64_tr_b8 %6, %14\n\tds_read_b64_tr_b8 %7, %15\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3]), "=&v"(a[4]), "=&v"(a[5]), "=&v"(a[6]),
+                       "=&v"(a[7])
+                     : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7])
+                     : "memory");
+    else
+        asm volatile("ds_read_b64_tr_b8 %0, %4\n\tds_read_b64_tr_b8 %1, %5\n\t"
+                     "ds_read_b64_tr_b8 %2, %6\n\tds_read_b64_tr_b8 %3, %7\n\t"
+                     "s_waitcnt lgkmcnt(0)"
+                     : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+                     : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+                     : "memory");
+}
 // N 16-byte LDS writes, complete before the block ends
 template <int N>
 __device__ __forceinline__ void lds_write_b128n(const unsigned (&p)[N], const u32x4 (&a)[N])
@@ -277,20 +331,20 @@ __device__ __forceinline__ void lds_write_b128n(const unsigned (&p)[N], const u3
                      : "memory");
 }
 
-// four FP8 E4M3 codes -> four bf16 (exact: every E4M3 value is a bf16 value)
+// four FP8 E4M3 codes -> four bf16 (exact: every E4M3 value is a bf16 value),
+// two codes per instruction (scale 1)
 __device__ __forceinline__ unsigned long long e4m3x4_to_bf16x4(unsigned w)
 {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
-    const bf16x4 r = __builtin_convertvector((f32x4{lo[0], lo[1], hi[0], hi[1]}), bf16x4);
-    return __builtin_bit_cast(unsigned long long, r);
+    const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, false);
+    const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, true);
+    return (unsigned long long)__builtin_bit_cast(unsigned, lo) | ((unsigned long long)__builtin_bit_cast(unsigned, hi) << 32);
 }
 
 template <int D, bool PAGED, bool KV8>
 __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
 {
     constexpr int NW = 4;
-    constexpr int TK = 16;                   // keys per tile
+    constexpr int TK = KV8 ? 32 : 16;        // keys per tile
     constexpr int ROWB = KV8 ? D : D * 2;    // bytes per cache row
     constexpr int QROWB = D * 2;             // bytes per query row (bf16)
     constexpr int CPR = ROWB / 16;           // 16-byte chunks per row
@@ -298,8 +352,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     constexpr int LOADS = TILEB / (64 * 16); // wave load instructions per tensor per tile
     constexpr int KS = D / 32;               // 16x16x32 k-steps over d
     constexpr int DB = D / 16;               // 16-row blocks of d for O^T
-    constexpr int VSTAGE = 2 * 2 * TILEB;    // FP8: bf16 copy of the V tile, after the two stages
-    constexpr int WAVE_LDS = 2 * 2 * TILEB + (KV8 ? TK * D * 2 : 0);
+    constexpr int WAVE_LDS = 2 * 2 * TILEB;  // two stages of a K and a V tile
     static_assert(TILEB % (64 * 16) == 0, "tile shape");
     static_assert(kDecodeHeadGroup == 16, "a workgroup serves up to 16 query heads (the 16x16 MFMA columns)");
 
@@ -336,7 +389,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         const int pos = i * 64 + lane;
         const int r = pos / CPR, cp = pos % CPR;
         ld_k[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : kswz<D>(r, cp)) * 16;
-        ld_v[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : dswz<D>(r, cp)) * 16;
+        ld_v[i] = r * ROWB + (KV8 ? vswz8<D>(r, cp) : dswz<D>(r, cp)) * 16;
     }
     // tile t of the chunk into stage s: rows past the chunk read as 0
     auto issue = [&](int t, int s) __attribute__((always_inline)) {
@@ -370,30 +423,24 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         else
             k_off[ks] = l16 * ROWB + kswz<D>(l16, 4 * ks + g4) * 16;
     }
-    // V^T fragments through transposing reads of a bf16 tile: the V tile of the
-    // stage, or (FP8) the wave's bf16 copy of it
+    // V^T fragments through transposing reads.  bf16: rows 4*g4 + l16/4 of
+    // the tile, two adjacent chunks of d block dm.  FP8 (32-key tiles): lane
+    // 16g + 2k + h reads 8 codes of row r_k (r_k = 4g + k for k < 4, 16 + 4g
+    // + k - 4 after), d = 16*dm + 8h .. +8; lane 16g + i then holds the codes
+    // of d = 16*dm + i for keys r_0..r_7, which are the keys this lane holds
+    // in P (4g..4g+3 of the first 16-key block of scores, 4g..4g+3 of the
+    // second)
     int v_off[DB];
-    {
+    if constexpr (KV8) {
+        const int kk = (lane & 15) >> 1;
+        const int r = kk < 4 ? 4 * g4 + kk : 16 + 4 * g4 + (kk - 4);
+#pragma unroll
+        for (int dm = 0; dm < DB; ++dm) v_off[dm] = TILEB + r * ROWB + vswz8<D>(r, dm) * 16 + (lane & 1) * 8;
+    } else {
         const int r = 4 * g4 + (l16 >> 2);
 #pragma unroll
         for (int dm = 0; dm < DB; ++dm)
-            v_off[dm] = (KV8 ? VSTAGE : TILEB) + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 +
-                        (l16 & 1) * 8;
-    }
-    // FP8: write i of lane l fills bytes 1024*i + 16*l of the wave's bf16 copy
-    // of the V tile (a linear write, free of bank conflicts); that position
-    // holds bf16 chunk dswz(row, position) of its row, whose 8 FP8 codes the
-    // lane reads first (one 8-byte read)
-    constexpr int NCV = TK * D * 2 / 1024;   // 16-byte writes per lane per tile
-    unsigned cv_src[NCV], cv_dst[NCV];
-    if constexpr (KV8) {
-#pragma unroll
-        for (int i = 0; i < NCV; ++i) {
-            const int byte = i * 1024 + lane * 16;
-            const int r = byte / QROWB, cc = dswz<D>(r, (byte % QROWB) / 16);
-            cv_dst[i] = VSTAGE + byte;
-            cv_src[i] = TILEB + r * ROWB + fswz<D>(r, cc >> 1) * 16 + (cc & 1) * 8;
-        }
+            v_off[dm] = TILEB + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 + (l16 & 1) * 8;
     }
 
     f32x4 oacc[DB];
@@ -428,55 +475,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     }
 
     const unsigned wl_addr = (unsigned)(uintptr_t)(LDS_AS char*)wl;
-    auto compute = [&](int t, int s) __attribute__((always_inline)) {
-        const unsigned st = wl_addr + s * 2 * TILEB;
-        bf16x8 kf[KS];
-        if constexpr (KV8) {
-            unsigned ka[KS];
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) ka[ks] = st + k_off[ks];
-            u32x2 k8[KS];
-            lds_read_b64n<KS>(k8, ka);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const unsigned long long lo = e4m3x4_to_bf16x4(k8[ks][0]), hi = e4m3x4_to_bf16x4(k8[ks][1]);
-                kf[ks] = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
-                                                           (unsigned)(hi >> 32)}));
-            }
-            // V tile: FP8 codes -> the wave's bf16 copy, laid out like a bf16 tile
-            unsigned va[NCV], wa[NCV];
-#pragma unroll
-            for (int i = 0; i < NCV; ++i) {
-                va[i] = st + cv_src[i];
-                wa[i] = wl_addr + cv_dst[i];
-            }
-            u32x2 v8[NCV];
-            u32x4 vb[NCV];
-            lds_read_b64n<NCV>(v8, va);
-#pragma unroll
-            for (int i = 0; i < NCV; ++i) {
-                const unsigned long long a = e4m3x4_to_bf16x4(v8[i][0]), c2 = e4m3x4_to_bf16x4(v8[i][1]);
-                vb[i] = u32x4{(unsigned)a, (unsigned)(a >> 32), (unsigned)c2, (unsigned)(c2 >> 32)};
-            }
-            lds_write_b128n<NCV>(wa, vb);
-        } else {
-            if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
-            else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
-        }
-        f32x4 sc = {};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
-        unsigned vaddr[DB];
-#pragma unroll
-        for (int dm = 0; dm < DB; ++dm) vaddr[dm] = (KV8 ? wl_addr : st) + v_off[dm];
-        i16x4 vf[DB];
-        if constexpr (DB == 8) lds_read_vt8(vf, vaddr);
-        else lds_read_vt4(vf, vaddr);
-        // keys past the chunk end
-        const int lim = nkeys - t * TK - 4 * g4;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sc[r] = (r < lim) ? sc[r] : kNegInf;
+    // online softmax of a lane's scores; returns their weights
+    auto online = [&](auto& sc) __attribute__((always_inline)) {
+        constexpr int N = sizeof(sc) / sizeof(float);
         float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+        if constexpr (N == 8) mx = fmaxf(mx, fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         mx = swap16_max(swap32_max(mx));
         const float m_blk = mx * p.c;
         if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kRescaleSlack)) {
@@ -488,14 +491,84 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
             m_run = m_new;
             nbase = (m_new == kNegInf) ? 0.f : -m_new;
         }
-        f32x4 e;
+    };
+    auto compute = [&](int t, int s) __attribute__((always_inline)) {
+        const unsigned st = wl_addr + s * 2 * TILEB;
+        if constexpr (KV8) {
+            // S^T of the two 16-key blocks of the tile; K codes -> bf16 (exact)
+            constexpr int NK = 2 * KS;
+            unsigned ka[NK];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
-        l_run += (e[0] + e[1]) + (e[2] + e[3]);
-        const bf16x4 pf = __builtin_convertvector(e, bf16x4);
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int dm = 0; dm < DB; ++dm)
-            oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vf[dm]), pf, oacc[dm], 0, 0, 0);
+                for (int ks = 0; ks < KS; ++ks) ka[kb * KS + ks] = st + k_off[ks] + kb * 16 * ROWB;
+            u32x2 k8[NK];
+            if constexpr (NK == 8) lds_read_b64x8(k8, ka);
+            else lds_read_b64n<4>(k8, ka);
+            unsigned vaddr[DB];
+#pragma unroll
+            for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
+            u32x2 v8[DB];
+            lds_read_tr8<DB>(v8, vaddr);
+            f32x4 sc2[2] = {f32x4{}, f32x4{}};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x2 w8 = k8[kb * KS + ks];
+                    const unsigned long long lo = e4m3x4_to_bf16x4(w8[0]), hi = e4m3x4_to_bf16x4(w8[1]);
+                    const bf16x8 kf = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
+                                                                         (unsigned)(hi >> 32)}));
+                    sc2[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sc2[kb], 0, 0, 0);
+                }
+            // keys past the chunk end: key 16*kb + 4*g4 + r of the tile
+            float sc[8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int lim = nkeys - t * TK - 16 * kb - 4 * g4;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[4 * kb + r] = (r < lim) ? sc2[kb][r] : kNegInf;
+            }
+            online(sc);
+            float e[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
+            l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+            const bf16x8 pf = __builtin_convertvector((f32x8{e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]}), bf16x8);
+#pragma unroll
+            for (int dm = 0; dm < DB; ++dm) {
+                const unsigned long long lo = e4m3x4_to_bf16x4(v8[dm][0]), hi = e4m3x4_to_bf16x4(v8[dm][1]);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
+                                                                     (unsigned)(hi >> 32)}));
+                oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dm], 0, 0, 0);
+            }
+        } else {
+            bf16x8 kf[KS];
+            if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
+            else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
+            f32x4 sc = {};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
+            unsigned vaddr[DB];
+#pragma unroll
+            for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
+            i16x4 vf[DB];
+            if constexpr (DB == 8) lds_read_vt8(vf, vaddr);
+            else lds_read_vt4(vf, vaddr);
+            // keys past the chunk end
+            const int lim = nkeys - t * TK - 4 * g4;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[r] = (r < lim) ? sc[r] : kNegInf;
+            online(sc);
+            f32x4 e;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
+            l_run += (e[0] + e[1]) + (e[2] + e[3]);
+            const bf16x4 pf = __builtin_convertvector(e, bf16x4);
+#pragma unroll
+            for (int dm = 0; dm < DB; ++dm)
+                oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vf[dm]), pf, oacc[dm], 0, 0, 0);
+        }
     };
 
     // ---- stream this wave's tiles: two in flight, no workgroup barrier
