@@ -596,31 +596,52 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     for (int dm = 0; dm < DB; ++dm)
         *reinterpret_cast<f32x4*>(sh_o + (w * 16 + l16) * D + (((4 * dm + g4) ^ l16) << 2)) = oacc[dm];
     __syncthreads();
-    for (int e = tid; e < nh * D; e += 256) {
-        const int hh = e / D, d = e % D;
-        float mm = kNegInf;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, sh_m[ww * 16 + hh]);
-        const float base = (mm == kNegInf) ? 0.f : mm;
-        float ll = 0.f, oo = 0.f;
+    // thread (head hh = tid/16, part q = tid%16): the 4-float chunks q and
+    // q+16 of the head's row (q alone at d = 64).  The head's 4 wave weights
+    // are computed once per thread, each chunk is one 16-byte read per wave
+    // (chunk positions q ^ hh: the 16 parts of a head cover all banks), and
+    // the 16 parts of a head store whole runs of the row.
+    constexpr int CH = D / 64;               // chunks per thread
+    const int hh = tid >> 4, q = tid & 15;
+    if (hh < nh) {
+        float mw[NW], mm = kNegInf;
 #pragma unroll
         for (int ww = 0; ww < NW; ++ww) {
-            const float mw = sh_m[ww * 16 + hh];
-            const float a = (mw == kNegInf) ? 0.f : fast_exp2(mw - base);
-            ll += a * sh_l[ww * 16 + hh];
-            oo += a * sh_o[(ww * 16 + hh) * D + ((((d >> 2) ^ hh)) << 2) + (d & 3)];
+            mw[ww] = sh_m[ww * 16 + hh];
+            mm = fmaxf(mm, mw[ww]);
         }
+        const float base = (mm == kNegInf) ? 0.f : mm;
+        float a[NW], ll = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) {
+            a[ww] = (mw[ww] == kNegInf) ? 0.f : fast_exp2(mw[ww] - base);
+            ll += a[ww] * sh_l[ww * 16 + hh];
+        }
+        const float scale_out = ll > 0.f ? p.v_scale / ll : 0.f;
         const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
-        const float val = ll > 0.f ? oo / ll * p.v_scale : 0.f;
-        const float lse_c = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
-        if (p.o) {
-            // S == 1 (row indexes (b, h)): the merge of one chunk has weight
-            // exactly 1, so this is the value it would write
-            p.o[row * D + d] = __builtin_bit_cast(uint16_t, __builtin_convertvector((f32x2{val, 0.f}), bf16x2)[0]);
-            if (d == 0 && p.lse) p.lse[row] = lse_c;
-        } else {
-            p.part_o[row * D + d] = val;
-            if (d == 0) p.part_lse[row] = lse_c;
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int c4 = q + 16 * k;       // chunk of the row: d = 4*c4 .. 4*c4+3
+            f32x4 oo = {};
+#pragma unroll
+            for (int ww = 0; ww < NW; ++ww)
+                oo += a[ww] * *reinterpret_cast<const f32x4*>(sh_o + (ww * 16 + hh) * D + ((c4 ^ hh) << 2));
+            const f32x4 val = oo * scale_out;
+            if (p.o) {
+                // S == 1 (row indexes (b, h)): the merge of one chunk has weight
+                // exactly 1, so this is the value it would write
+                *reinterpret_cast<bf16x4*>(p.o + row * D + 4 * c4) = __builtin_convertvector(val, bf16x4);
+            } else {
+                *reinterpret_cast<f32x4*>(p.part_o + row * D + 4 * c4) = val;
+            }
+        }
+        if (q == 0) {
+            const float lse_c = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
+            if (p.o) {
+                if (p.lse) p.lse[row] = lse_c;
+            } else {
+                p.part_lse[row] = lse_c;
+            }
         }
     }
 }
