@@ -568,6 +568,25 @@ def test_decode_fp8(H, H_kv, d, num_splits):
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("num_splits", [1, 3, 5])
+def test_decode_fp8_tile_boundaries(d, num_splits):
+    """The FP8 cache streams 32-key tiles, each two 16-key score blocks: lengths
+    and chunk ends on and around 16, 32, 48 and 64 keys (a tile whose second
+    block is empty, partly filled or whole), one query head per KV head and a
+    full group of 16."""
+    lens = np.array([1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 97, 160, 161], np.int32)
+    for H, H_kv in ((4, 4), (32, 2)):
+        spec = inputs.Decode(f"fp8_tiles_H{H}_Hkv{H_kv}_d{d}", len(lens), H, H_kv, d, 1, 200, 200, num_splits, 67,
+                             dtype="e4m3", k_scale=0.013, v_scale=2.0 ** -4)
+        say(f"fa_decode_fp8 tile boundaries {spec.name} S={num_splits}")
+        data = inputs.decode_inputs_fp8(spec, seq_lens=lens)
+        o, lse = _fp8_run(data, num_splits, spec.k_scale, spec.v_scale)
+        o_ref, lse_ref = oracle.decode_fp8(data.q, data.k_cache, data.v_cache, spec.k_scale, spec.v_scale, lens,
+                                           spec.scale)
+        compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
 def _random_cache_cases(n, seed=2026):
     rng = np.random.default_rng(seed)
     cases = []
