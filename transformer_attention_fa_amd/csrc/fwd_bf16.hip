@@ -57,15 +57,13 @@
 //    block streams into its own LDS area (spread over the item's periods,
 //    one slice per period when the item is long enough, all of it before the
 //    last period) and its first K tile into the K slot the last period
-//    leaves free.  After its last tile each wave takes its next Q
-//    fragments from that area, stages its finished 32 x d output tile in the
-//    same rows, and holds it in registers across the switch barrier; the
-//    whole-row stores issue after the barrier, so its wait for the next
-//    item's loads does not wait for them, and the next item's first period
-//    starts without waiting either;
+//    leaves free.  The item's last period (PV of its last tile) and the next
+//    item's first (S of its first tile) are one switch period: each wave
+//    takes its next Q fragments from that area, stages its finished 32 x d
+//    output tile in the same rows and stores it as whole rows, then starts
+//    the next item;
 //  * waves 0-3 take the block's later rows: on the causal diagonal those run
-//    longest, and a matrix-core-first wave ends with a lone PV phase, so the
-//    item's last period is short.
+//    longest, and the early-row waves finish before the switch period.
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -588,11 +586,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     //        waves 4-7:  softmax(j-1), MFMA(PV j-1, S j)
     //      A wave computes tiles a_w .. nkb_w-1: period a_w has no PV, period
     //      nkb_w no S, and the periods outside only keep the barriers and
-    //      loads.  Each role has its own loop (straight-line phases keep the
-    //      register allocation tight); all waves pass the same barriers.
-    //      Loads for the next item ride along: one slice of its Q block per
-    //      period (the rest in the last period) and its first K tile into the
-    //      K slot that the last period leaves free.
+    //      loads.  Periods kb_lo and nkb are switch periods (below), shared with
+    //      the item before and after.  Each role has its own loop (straight-line
+    //      phases keep the register allocation tight); all waves pass the same
+    //      barriers.  Loads for the next item ride along: qpp slices of its Q
+    //      block per period from period kb_lo+1 on, and its first K tile into
+    //      the K slot that period nkb-1 leaves free.
     // One period: the barrier, this period's loads into the free slots, then
     // the role's phases (SM: 1 = softmax of tile j-1 before the MFMAs, 2 =
     // softmax of tile j after them).  The slot pointers are restrict
