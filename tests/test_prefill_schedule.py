@@ -86,6 +86,9 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
             has_next, nxt = look_ahead(r)
             # prologue
             ev.append(('loadK', 0, (cur['id'], cur['kb_lo']), cur['kb_lo'] & 1)); bars += 1; period = 1
+            if role == 0:   # the first switch period's tiles, issued in the prologue
+                ev.append(('loadK', 0, (cur['id'], cur['kb_lo'] + 1), (cur['kb_lo'] & 1) ^ 1))
+                ev.append(('loadV', 0, (cur['id'], cur['kb_lo']), cur['kb_lo'] & 1))
             for part in range(8): ev.append(('loadQ', 0, cur['id'], part))
             def geom(it):
                 qw0 = it['q0'] + wr * 32
@@ -113,7 +116,7 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
                     period += 1; break
                 do_s = nkb_w > a_w and a_w == cur['kb_lo']
                 j = cur['kb_lo']
-                if role == 0:
+                if role == 0 and has_prev:
                     ldk = j + 1 < cur['nkb'] or (has_next and j == j_knext)
                     ktile = (cur['id'], j + 1) if j + 1 < cur['nkb'] else (nxt['id'], nxt['kb_lo'])
                     if ldk: ev.append(('loadK', period, ktile, mb ^ 1))

@@ -158,6 +158,13 @@ __device__ __forceinline__ void clock_stamp(unsigned long long* stamps, bool at_
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 // f(integral_constant<int, I>) for I = FIRST .. LAST-1, unrolled at compile time
 template <int FIRST, int LAST, typename F>
 __device__ __forceinline__ void static_for(F&& f)
@@ -817,7 +824,10 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                            const char* __restrict__ vt) __attribute__((always_inline)) {
         constexpr int RL = decltype(rolec)::value;
         static_assert(2 * (2 * LOADS0) <= mma_index(NPV, NSTEP), "the tile loads fit in the S product");
-        __builtin_amdgcn_s_waitcnt(0x0f70);
+        // the first switch period needs only the prologue's Q block and first
+        // K tile: waves 0-3 let their loads of the item's next tiles fly on
+        if (RL == 0 && !has_prev) wait_vmcnt<2 * LOADS0>();
+        else __builtin_amdgcn_s_waitcnt(0x0f70);
         __syncthreads();
         if constexpr (RL == 1) {
             if (do_pv) softmax_phase(j_last, CF{});      // with the finished item's rows
@@ -841,7 +851,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         if (!has_cur) return;
         const bool do_s = nkb_w > a_w && a_w == cur.kb_lo;
         const int j = cur.kb_lo;
-        const bool ldk = j + 1 < cur.nkb || (has_next && j == j_knext);
+        // (the first item's were issued in the prologue)
+        const bool ldv = has_prev;
+        const bool ldk = ldv && (j + 1 < cur.nkb || (has_next && j == j_knext));
         const i32x4 rk = j + 1 < cur.nkb ? tile_rsrc(kbase, j + 1)
                                         : tile_rsrc(reinterpret_cast<const char*>(p.k + (size_t)nxt.bg * (size_t)p.N_k * D), nxt.kb_lo);
         const i32x4 rv = tile_rsrc(vbase, j);
@@ -850,7 +862,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             if constexpr (i % 2 == 0 && i / 2 < LOADS0) {
                 if (ldk) issue0(rk, kdst, i / 2);
             } else if constexpr (i % 2 == 0 && i / 2 < 2 * LOADS0) {
-                issue0(rv, vdst, i / 2 - LOADS0);
+                if (ldv) issue0(rv, vdst, i / 2 - LOADS0);
             }
         };
         __builtin_amdgcn_sched_barrier(0);
@@ -864,7 +876,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 #pragma unroll
             for (int i = 0; i < LOADS0; ++i) {
                 if (ldk) issue0(rk, kdst, i);
-                issue0(rv, vdst, i);
+                if (ldv) issue0(rv, vdst, i);
             }
         }
         if constexpr (RL == 0) {
@@ -878,12 +890,24 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
                     lds + (2 + mb) * TILE, lds + mb * TILE, lds + (2 + (mb ^ 1)) * TILE);
     };
 
-    // prologue: the first item's Q block and first K tile
+    // prologue: the first item's Q block and first K tile (every wave), then
+    // its K tile kb_lo+1 and V tile kb_lo (waves 0-3, the loads of its first
+    // switch period, which waits for the first two only).  A K tile past the
+    // item (an item alone in its workgroup with one tile) loads as zeros or
+    // unused keys.
 #pragma unroll
     for (int part = 0; part < QPARTS; ++part) issue_q(cur, part);
     issue(reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D), cur.kb_lo, lds + (cur.kb_lo & 1) * TILE);
-    __builtin_amdgcn_s_waitcnt(0x0f70);
-    __syncthreads();
+    if (role == 0) {
+        const int mb0 = cur.kb_lo & 1;
+        const i32x4 rk = tile_rsrc(reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D), cur.kb_lo + 1);
+        const i32x4 rv = tile_rsrc(reinterpret_cast<const char*>(p.v + (size_t)cur.bg * (size_t)p.N_k * D), cur.kb_lo);
+#pragma unroll
+        for (int i = 0; i < LOADS0; ++i) {
+            issue0(rk, lds + (mb0 ^ 1) * TILE, i);
+            issue0(rv, lds + (2 + mb0) * TILE, i);
+        }
+    }
 
     // The item loop, compiled once per wave role (the two roles carry
     // different registers from period to period)
