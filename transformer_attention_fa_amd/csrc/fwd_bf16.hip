@@ -100,6 +100,30 @@ constexpr float kNegInf = -__builtin_inff();
 constexpr float kRescaleSlack = 8.0f;   // log2 units
 constexpr int kStreamOnce = 2;          // buffer load cache policy: non-temporal
 
+// n / d for 0 <= n < 2^31 as a multiply (high half) and a shift, for
+// launch-constant divisors (Granlund and Montgomery, "Division by invariant
+// integers using multiplication", 1994, the round-up method with N = 31):
+// m = ceil(2^(31+l) / d), l = ceil(log2 d), q = (n * m) >> (31 + l).  m = 0
+// marks d = 1.
+struct DivConst {
+    unsigned m;
+    unsigned s;   // l - 1
+};
+
+__host__ DivConst div_const(unsigned d)
+{
+    if (d <= 1) return {0u, 0u};
+    unsigned l = 0;
+    while ((1ull << l) < d) ++l;
+    const unsigned long long m = ((1ull << (31 + l)) + d - 1) / d;
+    return {(unsigned)m, l - 1};
+}
+
+__device__ __forceinline__ int div_by(int n, DivConst c)
+{
+    return c.m == 0 ? n : (int)(__umulhi((unsigned)n, c.m) >> c.s);
+}
+
 struct Params {
     const uint16_t* q;
     const uint16_t* k;
@@ -119,6 +143,11 @@ struct Params {
     // one per XCD, write {shader cycles, 100 MHz ticks, XCC id} at their start
     // and {shader cycles, ticks} at their end to stamps[8 * g .. 8 * g + 4]
     unsigned long long* stamps;
+    // the item decomposition's constants: the head list splits 8 ways
+    // (split8), nheads heads a list, groups of gsz heads (the last one glast,
+    // at index last_grp), and the divisors gsz * nqb, gsz, glast, H, rep
+    int split8, nheads, gsz, glast, last_grp;
+    DivConst div_gn, div_gsz, div_glast, div_h, div_rep;
 };
 
 // Race-hunting build (-DFA_DEBUG_BARRIERS): one more barrier in the middle
@@ -202,23 +231,21 @@ __device__ __forceinline__ int swz(int r, int c)
 // of `group` heads, longest causal query blocks first inside a group.
 __device__ __forceinline__ void decompose(int id, const Params& p, bool causal, int& qb, int& h, int& b)
 {
-    const int HB = p.H * p.B;
-    int head0 = 0, nheads = HB, slot = id;
-    if ((HB & 7) == 0) {
-        nheads = HB >> 3;
-        head0 = (id & 7) * nheads;
+    int head0 = 0, slot = id;
+    if (p.split8) {
+        head0 = (id & 7) * p.nheads;
         slot = id >> 3;
     }
-    const int gsz = min(p.group, nheads);
-    const int grp = slot / (gsz * p.nqb);
-    const int rem = slot - grp * gsz * p.nqb;
-    const int g0 = grp * gsz;
-    const int gcount = min(gsz, nheads - g0);
-    const int j = rem / gcount;
-    const int bh = head0 + g0 + rem % gcount;
+    const int grp = div_by(slot, p.div_gn);
+    const int rem = slot - grp * p.gsz * p.nqb;
+    const int g0 = grp * p.gsz;
+    const bool last = grp == p.last_grp;          // the last group may be smaller
+    const int gcount = last ? p.glast : p.gsz;
+    const int j = div_by(rem, last ? p.div_glast : p.div_gsz);
+    const int bh = head0 + g0 + rem - j * gcount;
     qb = causal ? p.nqb - 1 - j : j;
-    h = bh % p.H;
-    b = bh / p.H;
+    b = div_by(bh, p.div_h);
+    h = bh - b * p.H;
 }
 
 template <int D, int NW, bool CAUSAL, bool PERSIST, bool STAMPS>
@@ -308,7 +335,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
         decompose(id, p, CAUSAL, qb, h, b);
         Item it;
         it.bh = (unsigned)(b * p.H + h);
-        it.bg = (unsigned)(b * p.H_kv + h / p.rep);
+        it.bg = (unsigned)(b * p.H_kv + div_by(h, p.div_rep));
         it.q0 = qb * BM;
         int kend = p.N_k;
         if (CAUSAL) kend = min(p.N_k, it.q0 + BM + off);
@@ -1044,6 +1071,19 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     p.rep = a.H / a.H_kv;
     p.nqb = (a.N_q + BM - 1) / BM;
     p.group = group < 1 ? 1 : group;
+    {
+        const int HB = a.H * a.B;
+        p.split8 = (HB & 7) == 0;
+        p.nheads = p.split8 ? HB >> 3 : HB;
+        p.gsz = p.group < p.nheads ? p.group : p.nheads;
+        p.last_grp = (p.nheads - 1) / p.gsz;
+        p.glast = p.nheads - p.last_grp * p.gsz;
+        p.div_gn = div_const((unsigned)(p.gsz * p.nqb));
+        p.div_gsz = div_const((unsigned)p.gsz);
+        p.div_glast = div_const((unsigned)p.glast);
+        p.div_h = div_const((unsigned)a.H);
+        p.div_rep = div_const((unsigned)p.rep);
+    }
     p.window = CAUSAL ? a.window : 0;
     // scale 0 runs as a tiny positive scale: every exp2 argument then rounds to
     // 0 exactly as with scale 0, and masked scores stay -inf instead of NaN
