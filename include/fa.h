@@ -60,11 +60,12 @@
  *      fa_fwd_f32:             B * H * ceil(N_q / 64)  <= 2^31 - 1 at d = 128,
  *                              B * H * ceil(N_q / 128) <= 2^31 - 1 at d = 64;
  *      decode entry points:    B <= 65535, H_kv * ceil((H / H_kv) / 16) <= 65535,
- *                              B * H <= 2^31 - 4.
+ *                              B * H <= 2^31 - 4,
+ *                              num_splits * B * H_kv * ceil((H / H_kv) / 16) <= 2^31 - 1.
  *  - Thread safety: calls may come from any thread and keep no setting
  *    between calls.  The only process-wide state is the per-thread error
- *    message and a per-device cache of how many prefill workgroups fit on the
- *    device (filled once, the same value by every thread).
+ *    message and per-device caches of how many prefill and decode workgroups
+ *    fit on the device (filled once, the same value by every thread).
  */
 #ifndef FA_H
 #define FA_H
@@ -132,9 +133,10 @@ fa_status_t fa_fwd_f32(const float* q, const float* k, const float* v, float* o,
                        float scale, int causal, hipStream_t stream);
 
 /*
- * fa_decode_workspace_bytes -- size of the workspace fa_decode needs:
- * fp32 partial outputs [B,H,num_splits,d] followed by fp32 partial
- * log-sum-exps [B,H,num_splits].  Returns 0 for invalid arguments.
+ * fa_decode_workspace_bytes -- size of the workspace fa_decode needs: 256
+ * bytes holding the split kernel's chunk queue (an 8-byte word at the front),
+ * fp32 partial outputs [B,H,num_splits,d], then fp32 partial log-sum-exps
+ * [B,H,num_splits] (256-byte aligned).  Returns 0 for invalid arguments.
  */
 size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
 
@@ -167,7 +169,14 @@ size_t fa_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *   num_splits 1 .. 256
  *   workspace device buffer of at least fa_decode_workspace_bytes(B,H,d,num_splits)
  *             bytes, 16-byte aligned, owned by the caller; its contents on
- *             entry are ignored and on return are unspecified
+ *             entry are ignored and on return are unspecified, with one
+ *             exception: when num_splits > 1 and the chunks outnumber the
+ *             split workgroups that fit on the device, those workgroups take
+ *             chunks from a queue word at the front (a tag and a count).  The
+ *             merge kernel leaves it holding the tag and a zero count, and a
+ *             call that finds any other value starts the queue afresh; only
+ *             the tag with a nonzero count, which a call stopped between its
+ *             two kernels leaves, would be taken for a queue in progress
  *   stream    HIP stream; both kernels are enqueued on it, in order
  */
 fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
@@ -189,7 +198,9 @@ fa_status_t fa_decode(const void* q, const void* k_cache, const void* v_cache,
  *   FA_ERR_UNSUPPORTED before any launch.
  *   Every call on one GPU shares that GPU's array, and the array keeps the
  *   last call's contents.  Each call writes every partial it reads before
- *   reading it, so nothing needs clearing between calls.  Calls that overlap
+ *   reading it and leaves the chunk queue word ready for the next (the
+ *   array starts zeroed, which the first call takes for a fresh queue), so
+ *   nothing needs clearing between calls.  Calls that overlap
  *   on one GPU (on different streams, or from several threads) race on the
  *   array: serialise them, or use fa_decode with a workspace per stream.
  *   Other arguments, results and errors as fa_decode.

@@ -52,11 +52,14 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    B, H, d, S = 32, 32, 128, 16
-    o_bytes = B * H * S * d * 4
-    o_bytes = (o_bytes + 255) // 256 * 256
-    assert lib.fa_decode_workspace_bytes(B, H, d, S) == o_bytes + B * H * S * 4
-    assert lib.fa_decode_workspace_bytes(3, 5, 64, 7) == (3 * 5 * 7 * 64 * 4 + 255) // 256 * 256 + 3 * 5 * 7 * 4
+    # 256 bytes for the chunk queue word, partial outputs, then 256-byte
+    # aligned partial log-sum-exps
+    def expect(B, H, d, S):
+        rows = B * H * S
+        return 256 + (rows * d * 4 + 255) // 256 * 256 + rows * 4
+    assert lib.fa_decode_workspace_bytes(32, 32, 128, 16) == expect(32, 32, 128, 16)
+    assert lib.fa_decode_workspace_bytes(3, 5, 64, 7) == expect(3, 5, 64, 7)
+    assert expect(3, 5, 64, 7) == 256 + 26880 + 420
     for bad in [(0, 1, 64, 1), (1, 0, 64, 1), (1, 1, 0, 1), (1, 1, 64, 0), (1, 1, 64, 257)]:
         assert lib.fa_decode_workspace_bytes(*bad) == 0
 
@@ -301,6 +304,16 @@ def test_decode_row_limit(lib):
     assert 65535 * 32769 > (1 << 31) - 4
     assert _dec(lib, B=65535, H=32769, H_kv=32769, N_max=1, d=64, S=1, ws_bytes=1 << 40) == UNSUPPORTED
     assert b"B*H" in lib.fa_last_error()
+
+
+def test_decode_chunk_limit(lib):
+    # num_splits * B * head groups > 2^31 - 1 with every other count in range
+    assert 3 * 65535 * 16384 > (1 << 31) - 1 >= 2 * 65535 * 16384
+    assert _dec(lib, B=65535, H=16384, H_kv=16384, N_max=1, d=64, S=3, ws_bytes=1 << 40) == UNSUPPORTED
+    assert b"chunks" in lib.fa_last_error()
+    # two splits fit (then the workspace given is too small)
+    assert _dec(lib, B=65535, H=16384, H_kv=16384, N_max=1, d=64, S=2, ws_bytes=16) == INVALID
+    assert b"workspace" in lib.fa_last_error()
 
 
 def test_limits_apply_to_every_decode_entry(lib):

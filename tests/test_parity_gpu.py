@@ -803,6 +803,108 @@ def test_decode_deterministic_and_no_out_of_bounds_writes(num_splits):
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=f"guarded S={num_splits}")
 
 
+# ------------------------------------------------------------------ decode chunk queue
+# 32 sequences x 8 KV heads x 16 splits = 4096 chunks: more than the
+# workgroups that fit on the device at once, so the split kernel's resident
+# workgroups take chunks from the counter in the workspace.
+def _queue_spec(seed):
+    return inputs.Decode("decode_queue_B32_H16_Hkv8", 32, 16, 8, 128, 1, 640, 640, 16, seed)
+
+
+def _queue_run(spec, dev_lens, host_lens, ws, out=None, lse=None):
+    """Decode with device lengths dev_lens (0 = empty sequence) on caches drawn
+    for host_lens (1 where dev_lens is 0); returns the result and the oracle's."""
+    import torch
+    data = inputs.decode_inputs(spec, seq_lens=host_lens)
+    q = bf16_to_device(data.q)
+    kc, vc = bf16_to_device(data.k_cache), bf16_to_device(data.v_cache)
+    o, l = api.decode(q, kc, vc, torch.from_numpy(dev_lens).cuda(), num_splits=spec.num_splits, scale=spec.scale,
+                      workspace=ws, out=out, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, host_lens, spec.scale)
+    for b in np.nonzero(dev_lens == 0)[0]:
+        o_ref[b] = 0.0
+        lse_ref[b] = -np.inf
+    return o, l, o_ref, lse_ref
+
+
+# the queue word's tag (high half) as the library leaves it
+QUEUE_TAG = 0x46416451
+
+
+def test_decode_chunk_queue_garbage_and_reused_workspace():
+    """With the chunk queue in use, workspaces whose queue word the library did
+    not leave give the oracle's result: all bytes 0xff, the tag minus one with
+    an all-ones count (the first claim carries into the tag) and another tag
+    with a small count.  Each is followed by a second call on the same
+    workspace with other lengths: empty sequences, single keys and chunk edges
+    (chunks of 0, 1, 2 and 3 keys, 16-key tile edges)."""
+    import torch
+    spec = _queue_spec(89)
+    rng = np.random.default_rng(89)
+    lens_a = rng.integers(1, spec.N_max + 1, spec.B).astype(np.int32)
+    lens_b = lens_a.copy()
+    lens_b[:12] = [0, 0, 1, 2, 15, 16, 17, 33, 48, 257, 639, 640]
+    rng.shuffle(lens_b)
+    nbytes = api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits)
+    words = (("0xff bytes", None), ("tag - 1, count 2^32 - 1", ((QUEUE_TAG - 1) << 32) | 0xFFFFFFFF),
+             ("other tag, count 5", (0x12345678 << 32) | 5))
+    for name, word in words:
+        ws = torch.full((nbytes,), 255, dtype=torch.uint8, device="cuda")
+        if word is not None:
+            ws[:8].view(torch.int64).fill_(word - (1 << 64) if word >= 1 << 63 else word)
+        for label, dev_lens in ((f"{name}: first call", lens_a), (f"{name}: reused", lens_b)):
+            say(f"decode chunk queue, {label}")
+            o, lse, o_ref, lse_ref = _queue_run(spec, dev_lens, np.maximum(dev_lens, 1), ws)
+            compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=label)
+        # the merge left the queue idle: the tag and a zero count
+        torch.cuda.synchronize()
+        assert int(ws[:8].view(torch.int64).item()) == QUEUE_TAG << 32
+
+
+def test_decode_chunk_queue_graph_replays_match_eager():
+    """A decode step whose split kernel takes chunks from the queue (with the
+    kernel that zeroes the counter ahead of it), captured in a HIP graph,
+    replays to the eager result bit for bit, with eager calls on the same
+    workspace between the replays."""
+    import torch
+    spec = _queue_spec(97)
+    data = inputs.decode_inputs(spec)
+    q = bf16_to_device(data.q)
+    kc, vc = bf16_to_device(data.k_cache), bf16_to_device(data.v_cache)
+    lens = torch.from_numpy(data.seq_lens).cuda()
+    ws = torch.empty(api.decode_workspace_bytes(spec.B, spec.H, spec.d, spec.num_splits), dtype=torch.uint8,
+                     device="cuda")
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:-1], dtype=torch.float32, device="cuda")
+
+    def step():
+        api.decode(q, kc, vc, lens, num_splits=spec.num_splits, scale=spec.scale, out=o, lse=lse, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    ref = (o.clone(), lse.clone())
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, data.seq_lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label="eager decode")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g):
+            step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        o.fill_(float("nan"))
+        lse.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), ref[0].view(torch.int16)), rep
+        assert torch.equal(lse.view(torch.int32), ref[1].view(torch.int32)), rep
+        api.decode(q, kc, vc, lens, num_splits=spec.num_splits, scale=spec.scale, workspace=ws)
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ HIP graph capture
 def test_hip_graph_capture_replays_match_eager():
     """A prefill call and a decode step captured in one HIP graph (through

@@ -45,9 +45,11 @@ COMMON_FLAGS = [
 
 # per-source extras: the decode kernel rescales its accumulators in place, so
 # its matrix-core products accumulate in ordinary VGPRs rather than AGPRs
-# (which would need copies in and out on every rescale)
+# (which would need copies in and out on every rescale); and its one-lane
+# chunk-queue atomic stays a plain atomic (the atomic optimizer's wave
+# reduction would wait for the result at once, before the chunk's loads)
 EXTRA_FLAGS = {
-    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
 }
 
 

@@ -9,12 +9,17 @@
 // cache, so it is bound by memory bandwidth, and §2: a KV head serves
 // H/H_kv query heads).
 //
-// Split pass: workgroup (c, KV head and head group, b) takes keys
+// Split pass: chunk (c, KV head and head group, b) holds keys
 // [f + c*L, min(f + (c+1)*L, len)) with L = ceil((len - f) / num_splits), where
 // f = 0, or f = max(0, len - W) with a sliding window of W keys ("Attention
 // variants" §4: the newest token sees the W most recent rows), and serves up to 16
 // query heads that share one KV head, so each K/V byte of the chunk crosses HBM
-// once for all of them.  The chunk is cut into 16-key tiles (32 for FP8) dealt round robin
+// once for all of them.  A workgroup computes one chunk at a time.  When the
+// chunks outnumber the workgroups that fit on the device, the grid is one
+// resident set that takes chunks, longest sequence first, from a counter in
+// the workspace: the 8 XCDs stream at rates up to ~12 % apart, and chunks
+// dealt round robin (as the hardware deals workgroups) leave the fast XCDs
+// idle while the slow ones finish.  The chunk is cut into 16-key tiles (32 for FP8) dealt round robin
 // to the 4 waves; each wave streams its tiles into its own slice of LDS with
 // buffer_load_dwordx4 ... lds (two tiles in flight, no workgroup barrier) and
 // computes on the matrix cores:
@@ -44,6 +49,7 @@
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
+#include <atomic>
 #include <mutex>
 #include <cstdint>
 
@@ -96,7 +102,39 @@ struct SplitParams {
     // straight to o (bf16) and lse, and the merge kernel is not launched
     uint16_t* o;
     float* lse;
+    // chunks, in order: index = (rank of the sequence * H_kv * ngrp + head
+    // group) * S + chunk, longest sequences first.  Workgroup i takes chunk i;
+    // with a queue it then claims chunks grid, grid + 1, ... until none is
+    // left; without one grid == items.
+    int items, grid;
+    unsigned long long* queue;
 };
+
+// The chunk queue: one 64-bit word, tag in the high half and the number of
+// chunks claimed so far in the low half.  The merge kernel puts it back to
+// (kQueueTag, 0) after each launch that used it.  A word with another tag is
+// a workspace this library did not leave that way (its first use, or other
+// data): the first claim finds that and starts the queue afresh.
+constexpr unsigned long long kQueueTag = 0x46416451ull;   // "QdAF"
+constexpr unsigned long long kQueueIdle = kQueueTag << 32;
+
+// A claim is an add of 1 to the word, issued early; settle_claim(queue, old)
+// takes the word it returned and gives the index (0, 1, ...) of the claimed
+// chunk past the grid's first ones.
+__device__ __forceinline__ unsigned settle_claim(unsigned long long* queue, unsigned long long old)
+{
+    while ((old >> 32) != kQueueTag) {
+        // not a queue of this library: install (tag, 1), taking index 0.  Adds
+        // made to the stale word meanwhile are discarded with it; a workgroup
+        // that loses the race finds the tag and claims as usual.
+        const unsigned long long seen = old + 1;
+        const unsigned long long prev = atomicCAS(queue, seen, kQueueIdle | 1ull);
+        if (prev == seen) return 0;
+        if ((prev >> 32) == kQueueTag) old = atomicAdd(queue, 1ull);
+        else old = prev - 1;       // another stale add: retry against the word as it is
+    }
+    return (unsigned)old;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -153,6 +191,28 @@ __device__ __forceinline__ int vswz8(int r, int c)
 {
     if constexpr (D == 128) return c ^ (((r >> 1) & 3) | (((r >> 4) & 1) << 2));
     else return c ^ (((r >> 2) & 1) | (((r >> 4) & 1) << 1));
+}
+
+// Workgroup barrier for LDS traffic only: this wave's LDS reads and writes
+// complete, then s_barrier.  Unlike __syncthreads it does not wait for global
+// memory operations in flight (the partial stores, the chunk claim), which no
+// other wave of the workgroup reads.
+__device__ __forceinline__ void lds_barrier()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// An int from LDS, waiting for this read alone: a plain load there would make
+// the compiler wait for every vector memory operation in flight (it cannot
+// tell a global->LDS load, which could write the word, from the chunk claim).
+__device__ __forceinline__ int lds_read_int(const int* p)
+{
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)"
+                 : "=v"(v)
+                 : "v"((unsigned)(uintptr_t)(const LDS_AS int*)p)
+                 : "memory");
+    return v;
 }
 
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
@@ -238,26 +298,30 @@ __device__ __forceinline__ int key_start(const SplitParams& p, int len)
     return p.window > 0 ? max(0, len - p.window) : 0;
 }
 
-// Workgroups are dispatched in index order with blockIdx.z slowest, so z picks
-// the sequence by rank of length, longest first: the largest chunks start
-// first and the grid drains on the shortest ones.  Ranks order by length
-// (descending), then index, so they are a permutation of 0..B-1.  Batches of
-// more than 64 sequences keep index order.
-__device__ __forceinline__ int sequence_for(const SplitParams& p, int z)
+// Sequences are ranked by the keys they read (descending, then index), so
+// chunk indices run from the longest sequence to the shortest: the largest
+// chunks start first and the grid drains on the shortest ones.  Each lane
+// ranks sequence `lane` (ranks are a permutation of 0..B-1) from the
+// clamped lengths the lanes hold (lane_len); batches of more than 64
+// sequences keep index order.
+__device__ __forceinline__ int lane_rank(const SplitParams& p, int lane_len)
 {
-    if (p.B > 64) return z;
+    if (p.B > 64) return 0;
     const int lane = threadIdx.x & 63;
-    auto work = [&](int b) __attribute__((always_inline)) {   // keys the sequence reads
-        const int len = clamped_len(p, b);
-        return len - key_start(p, len);
-    };
-    const int mine = lane < p.B ? work(lane) : -1;
+    const int mine = lane < p.B ? lane_len - key_start(p, lane_len) : -1;
     int rank = 0;
     for (int j = 0; j < p.B; ++j) {
-        const int lj = work(j);
+        const int lj = __builtin_amdgcn_readlane(mine, j);
         rank += (lj > mine) || (lj == mine && j < lane);
     }
-    const uint64_t hit = __builtin_amdgcn_ballot_w64(lane < p.B && rank == z);
+    return rank;
+}
+
+// the sequence of rank z
+__device__ __forceinline__ int sequence_of_rank(const SplitParams& p, int rank, int z)
+{
+    if (p.B > 64) return z;
+    const uint64_t hit = __builtin_amdgcn_ballot_w64((int)(threadIdx.x & 63) < p.B && rank == z);
     return __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
 }
 
@@ -359,292 +423,322 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     constexpr int QB = 16 * 256;             // Q rows of the head group (16 x 256 B at most)
     __shared__ __attribute__((aligned(1024))) char lds[NW * WAVE_LDS + QB];
 
-    const int c = blockIdx.x;
-    const int g = blockIdx.y / p.ngrp;
-    const int hg = blockIdx.y % p.ngrp;
-    const int b = sequence_for(p, blockIdx.z);
-    const int h0 = g * p.rep + hg * 16;      // first query head of the group
-    const int nh = min(16, p.rep - hg * 16); // heads in the group
+    __shared__ int next_item;
+
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int l16 = lane & 15, g4 = lane >> 4;
+    // clamped length of sequence `lane`: read once, then taken from the lane
+    // that holds it (batches of at most 64 sequences)
+    const int lane_len = lane < min(p.B, 64) ? clamped_len(p, lane) : 0;
+    const int rank = lane_rank(p, lane_len);
+    const int gy = p.H_kv * p.ngrp;          // head groups per sequence
 
-    const int len = clamped_len(p, b);
-    const int kfirst = key_start(p, len);
-    int L = (len - kfirst + p.S - 1) / p.S;
-    if (PAGED) L = (L + TK - 1) / TK * TK;   // chunks and tiles start on page-aligned rows
-    const int j0 = kfirst + c * L;
-    const int nkeys = max(0, min(j0 + L, len) - j0);
-    const int ntiles = (nkeys + TK - 1) / TK;
-    const int nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles w, w+4, ...
+    for (int item = blockIdx.x; item < p.items;) {
+        const int c = item % p.S;
+        const int y = (item / p.S) % gy;
+        const int g = y / p.ngrp;
+        const int hg = y % p.ngrp;
+        const int b = sequence_of_rank(p, rank, item / (p.S * gy));
+        const int h0 = g * p.rep + hg * 16;      // first query head of the group
+        const int nh = min(16, p.rep - hg * 16); // heads in the group
 
-    const size_t kv_row0 = PAGED ? 0 : ((size_t)b * p.H_kv + g) * (size_t)p.N_max + (size_t)j0;
-    const char* kbase = p.k + kv_row0 * ROWB;
-    const char* vbase = p.v + kv_row0 * ROWB;
-    char* wl = lds + w * WAVE_LDS;
+        const int len = p.B <= 64 ? __builtin_amdgcn_readlane(lane_len, b) : clamped_len(p, b);
+        const int kfirst = key_start(p, len);
+        int L = (len - kfirst + p.S - 1) / p.S;
+        if (PAGED) L = (L + TK - 1) / TK * TK;   // chunks and tiles start on page-aligned rows
+        const int j0 = kfirst + c * L;
+        const int nkeys = max(0, min(j0 + L, len) - j0);
+        const int ntiles = (nkeys + TK - 1) / TK;
+        const int nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles w, w+4, ...
 
-    int ld_k[LOADS], ld_v[LOADS];
-#pragma unroll
-    for (int i = 0; i < LOADS; ++i) {
-        const int pos = i * 64 + lane;
-        const int r = pos / CPR, cp = pos % CPR;
-        ld_k[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : kswz<D>(r, cp)) * 16;
-        ld_v[i] = r * ROWB + (KV8 ? vswz8<D>(r, cp) : dswz<D>(r, cp)) * 16;
-    }
-    // tile t of the chunk into stage s: rows past the chunk read as 0
-    auto issue = [&](int t, int s) __attribute__((always_inline)) {
-        const int key0 = t * TK;
-        const unsigned bytes = (unsigned)min(TK, nkeys - key0) * ROWB;
-        size_t off = (size_t)key0 * ROWB;
-        if constexpr (PAGED) {
-            // the tile's 16 rows lie in one page (page_size % 16 == 0, aligned chunks)
-            const int row = j0 + key0;
-            const int blk = row / p.page_size;
-            int page = p.block_table[(size_t)b * p.max_blocks + blk];
-            page = min(max(page, 0), p.num_pages - 1);           // never outside the pool
-            off = (((size_t)page * p.H_kv + g) * p.page_size + (row - blk * p.page_size)) * ROWB;
-        }
-        const i32x4 rk = make_rsrc(kbase + off, bytes);
-        const i32x4 rv = make_rsrc(vbase + off, bytes);
-        char* dst = wl + s * 2 * TILEB;
-#pragma unroll
+        const size_t kv_row0 = PAGED ? 0 : ((size_t)b * p.H_kv + g) * (size_t)p.N_max + (size_t)j0;
+        const char* kbase = p.k + kv_row0 * ROWB;
+        const char* vbase = p.v + kv_row0 * ROWB;
+        char* wl = lds + w * WAVE_LDS;
+
+        int ld_k[LOADS], ld_v[LOADS];
+    #pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_k[i], 0, 0, kStreamPolicy);
-            fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_v[i], 0, 0, kStreamPolicy);
+            const int pos = i * 64 + lane;
+            const int r = pos / CPR, cp = pos % CPR;
+            ld_k[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : kswz<D>(r, cp)) * 16;
+            ld_v[i] = r * ROWB + (KV8 ? vswz8<D>(r, cp) : dswz<D>(r, cp)) * 16;
         }
-    };
+        // tile t of the chunk into stage s: rows past the chunk read as 0
+        auto issue = [&](int t, int s) __attribute__((always_inline)) {
+            const int key0 = t * TK;
+            const unsigned bytes = (unsigned)min(TK, nkeys - key0) * ROWB;
+            size_t off = (size_t)key0 * ROWB;
+            if constexpr (PAGED) {
+                // the tile's 16 rows lie in one page (page_size % 16 == 0, aligned chunks)
+                const int row = j0 + key0;
+                const int blk = row / p.page_size;
+                int page = p.block_table[(size_t)b * p.max_blocks + blk];
+                page = min(max(page, 0), p.num_pages - 1);           // never outside the pool
+                off = (((size_t)page * p.H_kv + g) * p.page_size + (row - blk * p.page_size)) * ROWB;
+            }
+            const i32x4 rk = make_rsrc(kbase + off, bytes);
+            const i32x4 rv = make_rsrc(vbase + off, bytes);
+            char* dst = wl + s * 2 * TILEB;
+    #pragma unroll
+            for (int i = 0; i < LOADS; ++i) {
+                fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_k[i], 0, 0, kStreamPolicy);
+                fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_v[i], 0, 0, kStreamPolicy);
+            }
+        };
 
-    // per-lane LDS read offsets inside a stage
-    int k_off[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (KV8)     // 8 bytes: d = 32*ks + 8*g4 .. +8 = half (g4 & 1) of chunk 2*ks + g4/2
-            k_off[ks] = l16 * ROWB + fswz<D>(l16, 2 * ks + (g4 >> 1)) * 16 + (g4 & 1) * 8;
-        else
-            k_off[ks] = l16 * ROWB + kswz<D>(l16, 4 * ks + g4) * 16;
-    }
-    // V^T fragments through transposing reads.  bf16: rows 4*g4 + l16/4 of
-    // the tile, two adjacent chunks of d block dm.  FP8 (32-key tiles): lane
-    // 16g + 2k + h reads 8 codes of row r_k (r_k = 4g + k for k < 4, 16 + 4g
-    // + k - 4 after), d = 16*dm + 8h .. +8; lane 16g + i then holds the codes
-    // of d = 16*dm + i for keys r_0..r_7, which are the keys this lane holds
-    // in P (4g..4g+3 of the first 16-key block of scores, 4g..4g+3 of the
-    // second)
-    int v_off[DB];
-    if constexpr (KV8) {
-        const int kk = (lane & 15) >> 1;
-        const int r = kk < 4 ? 4 * g4 + kk : 16 + 4 * g4 + (kk - 4);
-#pragma unroll
-        for (int dm = 0; dm < DB; ++dm) v_off[dm] = TILEB + r * ROWB + vswz8<D>(r, dm) * 16 + (lane & 1) * 8;
-    } else {
-        const int r = 4 * g4 + (l16 >> 2);
-#pragma unroll
-        for (int dm = 0; dm < DB; ++dm)
-            v_off[dm] = TILEB + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 + (l16 & 1) * 8;
-    }
-
-    f32x4 oacc[DB];
-#pragma unroll
-    for (int i = 0; i < DB; ++i) oacc[i] = f32x4{};
-    float m_run = kNegInf, nbase = 0.f, l_run = 0.f;
-
-    // ---- Q rows of the group into LDS (one 1 KB slice per wave; rows past the
-    // group read as 0; 16-byte chunks placed like a K tile row, whose fragment
-    // reads they repeat), then the first two tiles of this wave
-    char* qs = lds + NW * WAVE_LDS;
-    {
-        const int pos = w * 64 + lane;                  // 16-byte chunk position in the Q block
-        const int qr = pos / (QROWB / 16), qc = pos % (QROWB / 16);
-        const i32x4 rq = make_rsrc(p.q + ((size_t)b * p.H + h0) * D, (unsigned)nh * QROWB);
-        fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, qr * QROWB + kswz<D>(qr, qc) * 16, 0, 0, 0);
-    }
-    if (nt_w > 0) issue(w, 0);
-    if (nt_w > 1) issue(w + NW, 1);
-    if (nt_w > 1) wait_vmcnt<4 * LOADS>();      // the Q slice (older than both tiles) landed
-    else if (nt_w > 0) wait_vmcnt<2 * LOADS>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();               // every wave waited for its own slice
-    // Q^T fragments (B of S^T): head l16, d = 32*ks + 8*g4 .. +8 (chunk 4*ks + g4)
-    bf16x8 qf[KS];
-    {
-        const unsigned qa = (unsigned)(uintptr_t)(LDS_AS char*)qs + l16 * QROWB;
-        if constexpr (KS == 4)
-            lds_read_k4(qf, qa + kswz<D>(l16, g4) * 16, qa + kswz<D>(l16, 4 + g4) * 16, qa + kswz<D>(l16, 8 + g4) * 16,
-                        qa + kswz<D>(l16, 12 + g4) * 16);
-        else lds_read_k2(qf, qa + kswz<D>(l16, g4) * 16, qa + kswz<D>(l16, 4 + g4) * 16);
-    }
-
-    const unsigned wl_addr = (unsigned)(uintptr_t)(LDS_AS char*)wl;
-    // online softmax of a lane's scores; returns their weights
-    auto online = [&](auto& sc) __attribute__((always_inline)) {
-        constexpr int N = sizeof(sc) / sizeof(float);
-        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-        if constexpr (N == 8) mx = fmaxf(mx, fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        mx = swap16_max(swap32_max(mx));
-        const float m_blk = mx * p.c;
-        if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kRescaleSlack)) {
-            const float m_new = fmaxf(m_run, m_blk);
-            const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
-            l_run *= alpha;
-#pragma unroll
-            for (int dm = 0; dm < DB; ++dm) oacc[dm] *= alpha;
-            m_run = m_new;
-            nbase = (m_new == kNegInf) ? 0.f : -m_new;
+        // per-lane LDS read offsets inside a stage
+        int k_off[KS];
+    #pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            if constexpr (KV8)     // 8 bytes: d = 32*ks + 8*g4 .. +8 = half (g4 & 1) of chunk 2*ks + g4/2
+                k_off[ks] = l16 * ROWB + fswz<D>(l16, 2 * ks + (g4 >> 1)) * 16 + (g4 & 1) * 8;
+            else
+                k_off[ks] = l16 * ROWB + kswz<D>(l16, 4 * ks + g4) * 16;
         }
-    };
-    auto compute = [&](int t, int s) __attribute__((always_inline)) {
-        const unsigned st = wl_addr + s * 2 * TILEB;
+        // V^T fragments through transposing reads.  bf16: rows 4*g4 + l16/4 of
+        // the tile, two adjacent chunks of d block dm.  FP8 (32-key tiles): lane
+        // 16g + 2k + h reads 8 codes of row r_k (r_k = 4g + k for k < 4, 16 + 4g
+        // + k - 4 after), d = 16*dm + 8h .. +8; lane 16g + i then holds the codes
+        // of d = 16*dm + i for keys r_0..r_7, which are the keys this lane holds
+        // in P (4g..4g+3 of the first 16-key block of scores, 4g..4g+3 of the
+        // second)
+        int v_off[DB];
         if constexpr (KV8) {
-            // S^T of the two 16-key blocks of the tile; K codes -> bf16 (exact)
-            constexpr int NK = 2 * KS;
-            unsigned ka[NK];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) ka[kb * KS + ks] = st + k_off[ks] + kb * 16 * ROWB;
-            u32x2 k8[NK];
-            if constexpr (NK == 8) lds_read_b64x8(k8, ka);
-            else lds_read_b64n<4>(k8, ka);
-            unsigned vaddr[DB];
-#pragma unroll
-            for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
-            u32x2 v8[DB];
-            lds_read_tr8<DB>(v8, vaddr);
-            f32x4 sc2[2] = {f32x4{}, f32x4{}};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < KS; ++ks) {
-                    const u32x2 w8 = k8[kb * KS + ks];
-                    const unsigned long long lo = e4m3x4_to_bf16x4(w8[0]), hi = e4m3x4_to_bf16x4(w8[1]);
-                    const bf16x8 kf = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
-                                                                         (unsigned)(hi >> 32)}));
-                    sc2[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sc2[kb], 0, 0, 0);
-                }
-            // keys past the chunk end: key 16*kb + 4*g4 + r of the tile
-            float sc[8];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int lim = nkeys - t * TK - 16 * kb - 4 * g4;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[4 * kb + r] = (r < lim) ? sc2[kb][r] : kNegInf;
-            }
-            online(sc);
-            float e[8];
-#pragma unroll
-            for (int r = 0; r < 8; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
-            l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-            const bf16x8 pf = __builtin_convertvector((f32x8{e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]}), bf16x8);
-#pragma unroll
-            for (int dm = 0; dm < DB; ++dm) {
-                const unsigned long long lo = e4m3x4_to_bf16x4(v8[dm][0]), hi = e4m3x4_to_bf16x4(v8[dm][1]);
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
-                                                                     (unsigned)(hi >> 32)}));
-                oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dm], 0, 0, 0);
-            }
+            const int kk = (lane & 15) >> 1;
+            const int r = kk < 4 ? 4 * g4 + kk : 16 + 4 * g4 + (kk - 4);
+    #pragma unroll
+            for (int dm = 0; dm < DB; ++dm) v_off[dm] = TILEB + r * ROWB + vswz8<D>(r, dm) * 16 + (lane & 1) * 8;
         } else {
-            bf16x8 kf[KS];
-            if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
-            else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
-            f32x4 sc = {};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
-            unsigned vaddr[DB];
-#pragma unroll
-            for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
-            i16x4 vf[DB];
-            if constexpr (DB == 8) lds_read_vt8(vf, vaddr);
-            else lds_read_vt4(vf, vaddr);
-            // keys past the chunk end
-            const int lim = nkeys - t * TK - 4 * g4;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[r] = (r < lim) ? sc[r] : kNegInf;
-            online(sc);
-            f32x4 e;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
-            l_run += (e[0] + e[1]) + (e[2] + e[3]);
-            const bf16x4 pf = __builtin_convertvector(e, bf16x4);
-#pragma unroll
+            const int r = 4 * g4 + (l16 >> 2);
+    #pragma unroll
             for (int dm = 0; dm < DB; ++dm)
-                oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vf[dm]), pf, oacc[dm], 0, 0, 0);
+                v_off[dm] = TILEB + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 + (l16 & 1) * 8;
         }
-    };
 
-    // ---- stream this wave's tiles: two in flight, no workgroup barrier
-    for (int i = 0; i < nt_w; ++i) {
-        if (i + 1 < nt_w) wait_vmcnt<2 * LOADS>();     // tile i landed, tile i+1 may still fly
+        f32x4 oacc[DB];
+    #pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[i] = f32x4{};
+        float m_run = kNegInf, nbase = 0.f, l_run = 0.f;
+
+        // ---- Q rows of the group into LDS (one 1 KB slice per wave; rows past the
+        // group read as 0; 16-byte chunks placed like a K tile row, whose fragment
+        // reads they repeat), then the first two tiles of this wave
+        char* qs = lds + NW * WAVE_LDS;
+        {
+            const int pos = w * 64 + lane;                  // 16-byte chunk position in the Q block
+            const int qr = pos / (QROWB / 16), qc = pos % (QROWB / 16);
+            const i32x4 rq = make_rsrc(p.q + ((size_t)b * p.H + h0) * D, (unsigned)nh * QROWB);
+            fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, qr * QROWB + kswz<D>(qr, qc) * 16, 0, 0, 0);
+        }
+        if (nt_w > 0) issue(w, 0);
+        if (nt_w > 1) issue(w + NW, 1);
+        if (nt_w > 1) wait_vmcnt<4 * LOADS>();      // the Q slice (older than both tiles) landed
+        else if (nt_w > 0) wait_vmcnt<2 * LOADS>();
         else wait_vmcnt<0>();
-        compute(w + i * NW, i & 1);
-        if (i + 2 < nt_w) issue(w + (i + 2) * NW, i & 1);   // this stage's reads are complete
-    }
+        __builtin_amdgcn_s_barrier();               // every wave waited for its own slice
+        // Q^T fragments (B of S^T): head l16, d = 32*ks + 8*g4 .. +8 (chunk 4*ks + g4)
+        bf16x8 qf[KS];
+        {
+            const unsigned qa = (unsigned)(uintptr_t)(LDS_AS char*)qs + l16 * QROWB;
+            if constexpr (KS == 4)
+                lds_read_k4(qf, qa + kswz<D>(l16, g4) * 16, qa + kswz<D>(l16, 4 + g4) * 16, qa + kswz<D>(l16, 8 + g4) * 16,
+                            qa + kswz<D>(l16, 12 + g4) * 16);
+            else lds_read_k2(qf, qa + kswz<D>(l16, g4) * 16, qa + kswz<D>(l16, 4 + g4) * 16);
+        }
 
-    // ---- merge the 4 waves through LDS and write the chunk's partial result
-    const float l_head = swap16_sum(swap32_sum(l_run));      // sum over the 4 key groups
-    __syncthreads();                                          // tile slices are free
-    float* sh_m = reinterpret_cast<float*>(lds);             // [NW][16]
-    float* sh_l = sh_m + NW * 16;                             // [NW][16]
-    float* sh_o = sh_l + NW * 16;                             // [NW][16][D]
-    if (g4 == 0) {
-        sh_m[w * 16 + l16] = m_run;
-        sh_l[w * 16 + l16] = l_head;
-    }
-    // row (w, head l16): the 4 accumulator values of d-block dm are 16
-    // contiguous bytes, chunk 4*dm + g4 of the row; the chunk index is XORed
-    // with the head so the 16 heads of one write land in different banks
-#pragma unroll
-    for (int dm = 0; dm < DB; ++dm)
-        *reinterpret_cast<f32x4*>(sh_o + (w * 16 + l16) * D + (((4 * dm + g4) ^ l16) << 2)) = oacc[dm];
-    __syncthreads();
-    // thread (head hh = tid/16, part q = tid%16): the 4-float chunks q and
-    // q+16 of the head's row (q alone at d = 64).  The head's 4 wave weights
-    // are computed once per thread, each chunk is one 16-byte read per wave
-    // (chunk positions q ^ hh: the 16 parts of a head cover all banks), and
-    // the 16 parts of a head store whole runs of the row.
-    constexpr int CH = D / 64;               // chunks per thread
-    const int hh = tid >> 4, q = tid & 15;
-    if (hh < nh) {
-        float mw[NW], mm = kNegInf;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            mw[ww] = sh_m[ww * 16 + hh];
-            mm = fmaxf(mm, mw[ww]);
-        }
-        const float base = (mm == kNegInf) ? 0.f : mm;
-        float a[NW], ll = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < NW; ++ww) {
-            a[ww] = (mw[ww] == kNegInf) ? 0.f : fast_exp2(mw[ww] - base);
-            ll += a[ww] * sh_l[ww * 16 + hh];
-        }
-        const float scale_out = ll > 0.f ? p.v_scale / ll : 0.f;
-        const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
-#pragma unroll
-        for (int k = 0; k < CH; ++k) {
-            const int c4 = q + 16 * k;       // chunk of the row: d = 4*c4 .. 4*c4+3
-            f32x4 oo = {};
-#pragma unroll
-            for (int ww = 0; ww < NW; ++ww)
-                oo += a[ww] * *reinterpret_cast<const f32x4*>(sh_o + (ww * 16 + hh) * D + ((c4 ^ hh) << 2));
-            const f32x4 val = oo * scale_out;
-            if (p.o) {
-                // S == 1 (row indexes (b, h)): the merge of one chunk has weight
-                // exactly 1, so this is the value it would write
-                *reinterpret_cast<bf16x4*>(p.o + row * D + 4 * c4) = __builtin_convertvector(val, bf16x4);
+        const unsigned wl_addr = (unsigned)(uintptr_t)(LDS_AS char*)wl;
+        // online softmax of a lane's scores; returns their weights
+        auto online = [&](auto& sc) __attribute__((always_inline)) {
+            constexpr int N = sizeof(sc) / sizeof(float);
+            float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            if constexpr (N == 8) mx = fmaxf(mx, fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            mx = swap16_max(swap32_max(mx));
+            const float m_blk = mx * p.c;
+            if (__builtin_amdgcn_ballot_w64(m_blk > m_run + kRescaleSlack)) {
+                const float m_new = fmaxf(m_run, m_blk);
+                const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
+                l_run *= alpha;
+    #pragma unroll
+                for (int dm = 0; dm < DB; ++dm) oacc[dm] *= alpha;
+                m_run = m_new;
+                nbase = (m_new == kNegInf) ? 0.f : -m_new;
+            }
+        };
+        auto compute = [&](int t, int s) __attribute__((always_inline)) {
+            const unsigned st = wl_addr + s * 2 * TILEB;
+            if constexpr (KV8) {
+                // S^T of the two 16-key blocks of the tile; K codes -> bf16 (exact)
+                constexpr int NK = 2 * KS;
+                unsigned ka[NK];
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) ka[kb * KS + ks] = st + k_off[ks] + kb * 16 * ROWB;
+                u32x2 k8[NK];
+                if constexpr (NK == 8) lds_read_b64x8(k8, ka);
+                else lds_read_b64n<4>(k8, ka);
+                unsigned vaddr[DB];
+    #pragma unroll
+                for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
+                u32x2 v8[DB];
+                lds_read_tr8<DB>(v8, vaddr);
+                f32x4 sc2[2] = {f32x4{}, f32x4{}};
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+    #pragma unroll
+                    for (int ks = 0; ks < KS; ++ks) {
+                        const u32x2 w8 = k8[kb * KS + ks];
+                        const unsigned long long lo = e4m3x4_to_bf16x4(w8[0]), hi = e4m3x4_to_bf16x4(w8[1]);
+                        const bf16x8 kf = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
+                                                                             (unsigned)(hi >> 32)}));
+                        sc2[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], sc2[kb], 0, 0, 0);
+                    }
+                // keys past the chunk end: key 16*kb + 4*g4 + r of the tile
+                float sc[8];
+    #pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int lim = nkeys - t * TK - 16 * kb - 4 * g4;
+    #pragma unroll
+                    for (int r = 0; r < 4; ++r) sc[4 * kb + r] = (r < lim) ? sc2[kb][r] : kNegInf;
+                }
+                online(sc);
+                float e[8];
+    #pragma unroll
+                for (int r = 0; r < 8; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
+                l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+                const bf16x8 pf = __builtin_convertvector((f32x8{e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]}), bf16x8);
+    #pragma unroll
+                for (int dm = 0; dm < DB; ++dm) {
+                    const unsigned long long lo = e4m3x4_to_bf16x4(v8[dm][0]), hi = e4m3x4_to_bf16x4(v8[dm][1]);
+                    const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
+                                                                         (unsigned)(hi >> 32)}));
+                    oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf, oacc[dm], 0, 0, 0);
+                }
             } else {
-                *reinterpret_cast<f32x4*>(p.part_o + row * D + 4 * c4) = val;
+                bf16x8 kf[KS];
+                if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
+                else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
+                f32x4 sc = {};
+    #pragma unroll
+                for (int ks = 0; ks < KS; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
+                unsigned vaddr[DB];
+    #pragma unroll
+                for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
+                i16x4 vf[DB];
+                if constexpr (DB == 8) lds_read_vt8(vf, vaddr);
+                else lds_read_vt4(vf, vaddr);
+                // keys past the chunk end
+                const int lim = nkeys - t * TK - 4 * g4;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) sc[r] = (r < lim) ? sc[r] : kNegInf;
+                online(sc);
+                f32x4 e;
+    #pragma unroll
+                for (int r = 0; r < 4; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
+                l_run += (e[0] + e[1]) + (e[2] + e[3]);
+                const bf16x4 pf = __builtin_convertvector(e, bf16x4);
+    #pragma unroll
+                for (int dm = 0; dm < DB; ++dm)
+                    oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vf[dm]), pf, oacc[dm], 0, 0, 0);
+            }
+        };
+
+        // ---- stream this wave's tiles: two in flight, no workgroup barrier.
+        // Wave 0 claims the chunk after this one just behind its last tile's
+        // loads: late enough that the chunk it takes is not held back from
+        // other workgroups for long, early enough that the atomic's round trip
+        // overlaps the last tile.  The wait for the tile before the last
+        // allows for it (one more operation in flight).
+        const bool claiming = p.queue && w == 0;
+        unsigned long long claim = 0;
+        for (int i = 0; i < nt_w; ++i) {
+            if (i + 1 < nt_w) {                           // tile i landed, tile i+1 may still fly
+                if (claiming && i + 2 == nt_w && nt_w >= 3) wait_vmcnt<2 * LOADS + 1>();   // and the claim
+                else wait_vmcnt<2 * LOADS>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            compute(w + i * NW, i & 1);
+            if (i + 2 < nt_w) issue(w + (i + 2) * NW, i & 1);   // this stage's reads are complete
+            if (claiming && i + 3 == nt_w && lane == 0) claim = atomicAdd(p.queue, 1ull);
+        }
+        if (claiming && nt_w < 3 && lane == 0) claim = atomicAdd(p.queue, 1ull);
+
+        // ---- merge the 4 waves through LDS and write the chunk's partial result
+        const float l_head = swap16_sum(swap32_sum(l_run));      // sum over the 4 key groups
+        lds_barrier();                                            // tile slices are free
+        float* sh_m = reinterpret_cast<float*>(lds);             // [NW][16]
+        float* sh_l = sh_m + NW * 16;                             // [NW][16]
+        float* sh_o = sh_l + NW * 16;                             // [NW][16][D]
+        if (g4 == 0) {
+            sh_m[w * 16 + l16] = m_run;
+            sh_l[w * 16 + l16] = l_head;
+        }
+        // row (w, head l16): the 4 accumulator values of d-block dm are 16
+        // contiguous bytes, chunk 4*dm + g4 of the row; the chunk index is XORed
+        // with the head so the 16 heads of one write land in different banks
+    #pragma unroll
+        for (int dm = 0; dm < DB; ++dm)
+            *reinterpret_cast<f32x4*>(sh_o + (w * 16 + l16) * D + (((4 * dm + g4) ^ l16) << 2)) = oacc[dm];
+        lds_barrier();
+        // thread (head hh = tid/16, part q = tid%16): the 4-float chunks q and
+        // q+16 of the head's row (q alone at d = 64).  The head's 4 wave weights
+        // are computed once per thread, each chunk is one 16-byte read per wave
+        // (chunk positions q ^ hh: the 16 parts of a head cover all banks), and
+        // the 16 parts of a head store whole runs of the row.
+        constexpr int CH = D / 64;               // chunks per thread
+        const int hh = tid >> 4, q = tid & 15;
+        if (hh < nh) {
+            float mw[NW], mm = kNegInf;
+    #pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                mw[ww] = sh_m[ww * 16 + hh];
+                mm = fmaxf(mm, mw[ww]);
+            }
+            const float base = (mm == kNegInf) ? 0.f : mm;
+            float a[NW], ll = 0.f;
+    #pragma unroll
+            for (int ww = 0; ww < NW; ++ww) {
+                a[ww] = (mw[ww] == kNegInf) ? 0.f : fast_exp2(mw[ww] - base);
+                ll += a[ww] * sh_l[ww * 16 + hh];
+            }
+            const float scale_out = ll > 0.f ? p.v_scale / ll : 0.f;
+            const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
+    #pragma unroll
+            for (int k = 0; k < CH; ++k) {
+                const int c4 = q + 16 * k;       // chunk of the row: d = 4*c4 .. 4*c4+3
+                f32x4 oo = {};
+    #pragma unroll
+                for (int ww = 0; ww < NW; ++ww)
+                    oo += a[ww] * *reinterpret_cast<const f32x4*>(sh_o + (ww * 16 + hh) * D + ((c4 ^ hh) << 2));
+                const f32x4 val = oo * scale_out;
+                if (p.o) {
+                    // S == 1 (row indexes (b, h)): the merge of one chunk has weight
+                    // exactly 1, so this is the value it would write
+                    *reinterpret_cast<bf16x4*>(p.o + row * D + 4 * c4) = __builtin_convertvector(val, bf16x4);
+                } else {
+                    *reinterpret_cast<f32x4*>(p.part_o + row * D + 4 * c4) = val;
+                }
+            }
+            if (q == 0) {
+                const float lse_c = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
+                if (p.o) {
+                    if (p.lse) p.lse[row] = lse_c;
+                } else {
+                    p.part_lse[row] = lse_c;
+                }
             }
         }
-        if (q == 0) {
-            const float lse_c = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
-            if (p.o) {
-                if (p.lse) p.lse[row] = lse_c;
-            } else {
-                p.part_lse[row] = lse_c;
-            }
-        }
+        if (tid == 0)
+            next_item = p.queue ? (int)min((long long)p.grid + settle_claim(p.queue, claim), (long long)p.items)
+                                : p.items;
+        lds_barrier();               // the tile slices, the Q block and the merge area are free again
+        item = __builtin_amdgcn_readfirstlane(lds_read_int(&next_item));
     }
 }
+
 
 struct CombineParams {
     const float* part_o;
@@ -653,6 +747,7 @@ struct CombineParams {
     float* lse;
     int rows;     // B*H
     int S;
+    unsigned long long* queue;   // the split launch's chunk queue, or null
 };
 
 // One wave per (b, h) row: merge the S chunk summaries by their log-sum-exp.
@@ -670,6 +765,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p)
     typedef float vecP __attribute__((ext_vector_type(PER)));
     const int row = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
+    // the split kernel has finished: leave its queue ready for the next launch
+    if (p.queue && blockIdx.x == 0 && threadIdx.x == 0) atomicExch(p.queue, kQueueIdle);
     if (row >= p.rows) return;
     const int S = p.S;                   // 1..256; chunk indices past S are clamped and weigh 0
     const float* lse_c = p.part_lse + (size_t)row * S;
@@ -735,6 +832,25 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p)
     if (p.lse && lane == 0) p.lse[row] = lse;
 }
 
+// Workgroups of a kernel that fit on the current device at once.  Cached per
+// device and kernel (host threads may race to fill an entry; they store the
+// same value); 0 if the runtime cannot say.
+template <typename K>
+int resident_blocks(K kernel, int threads)
+{
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    const int known = cache[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    const int n = cus * (per_cu > 0 ? per_cu : 1);
+    cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 template <int D, bool PAGED, bool KV8>
 hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
 {
@@ -762,11 +878,25 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     p.v_scale = KV8 ? a.v_scale : 1.f;
     p.o = a.num_splits == 1 ? static_cast<uint16_t*>(a.o) : nullptr;
     p.lse = a.lse;
-    const long long gy = (long long)a.H_kv * p.ngrp;   // gy and B at most 65535: checked on the host
-    hipLaunchKernelGGL((decode_split_kernel<D, PAGED, KV8>), dim3(a.num_splits, (unsigned)gy, a.B), dim3(256), 0, stream, p);
+    // chunks (at most 2^31 - 1: checked on the host)
+    p.items = (int)((long long)a.num_splits * a.H_kv * p.ngrp * a.B);
+    // With several chunks per sequence and more chunks than fit on the device
+    // at once, the grid is one resident set of workgroups that take chunks from
+    // a queue in the workspace: the XCDs stream at different rates, and the
+    // fixed round-robin spread of a one-chunk-a-workgroup grid leaves the fast
+    // ones idle at the end.  Otherwise every chunk is a workgroup of its own.
+    const int resident = resident_blocks(decode_split_kernel<D, PAGED, KV8>, 256);
+    if (a.num_splits > 1 && a.queue && resident > 0 && p.items > resident) {
+        p.grid = resident;
+        p.queue = a.queue;
+    } else {
+        p.grid = p.items;
+        p.queue = nullptr;
+    }
+    hipLaunchKernelGGL((decode_split_kernel<D, PAGED, KV8>), dim3(p.grid), dim3(256), 0, stream, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.num_splits == 1) return e;
-    CombineParams cp{a.part_o, a.part_lse, static_cast<uint16_t*>(a.o), a.lse, a.B * a.H, a.num_splits};
+    CombineParams cp{a.part_o, a.part_lse, static_cast<uint16_t*>(a.o), a.lse, a.B * a.H, a.num_splits, p.queue};
     hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((cp.rows + 3) / 4), dim3(256), 0, stream, cp);
     return hipGetLastError();
 }

@@ -83,14 +83,24 @@ fa_status_t from_hip(hipError_t e, const char* what)
     return fail(FA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Workspace layout: the split kernel's chunk queue (one 64-bit word) at the
+// front, on 256 bytes of its own, so it sits in the same place whatever the
+// shape of the call; then fp32 partial outputs [B,H,S,d] and 256-byte aligned
+// fp32 partial log-sum-exps [B,H,S].
+constexpr size_t kQueueBytes = 256;
+
+size_t workspace_lse_offset(int B, int H, int d, int num_splits)
+{
+    const size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
+    return kQueueBytes + (rows * (size_t)d * sizeof(float) + 255) / 256 * 256;
+}
+
 size_t workspace_bytes_for(int B, int H, int d, int num_splits)
 {
     if (B < 1 || H < 1 || d < 1 || num_splits < 1 || num_splits > 256) return 0;
     if (too_large(B, H, num_splits, d + 1)) return 0;
-    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
-    size_t o_bytes = rows * (size_t)d * sizeof(float);
-    o_bytes = (o_bytes + 255) / 256 * 256;           // partial lse starts 256-byte aligned
-    return o_bytes + rows * sizeof(float);
+    const size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
+    return workspace_lse_offset(B, H, d, num_splits) + rows * sizeof(float);
 }
 
 fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cache,
@@ -104,8 +114,9 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
 {
     fa_status_t s = check_common(q, k_cache, v_cache, o, lse, B, H, H_kv, 1, N_max, d, scale);
     if (s != FA_OK) return s;
-    // grid limits: the split kernel runs (num_splits, H_kv * ceil(rep / 16),
-    // B) workgroups, the merge one workgroup per 4 (b, h) rows
+    // grid limits: the split kernel takes num_splits * H_kv * ceil(rep / 16)
+    // * B chunks (a one-dimensional grid of up to that many workgroups), the
+    // merge one workgroup per 4 (b, h) rows
     const long long head_groups = (long long)H_kv * ((H / H_kv + fa::kDecodeHeadGroup - 1) / fa::kDecodeHeadGroup);
     if (B > fa::kMaxGridYZ)
         return fail(FA_ERR_UNSUPPORTED, "%s: B=%d sequences exceed the %lld a launch can take", name, B,
@@ -116,6 +127,9 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
     if ((long long)B * H > fa::kMaxGridX - 3)
         return fail(FA_ERR_UNSUPPORTED, "%s: B*H = %lld query rows exceed %lld", name, (long long)B * H,
                     fa::kMaxGridX - 3);
+    if (num_splits >= 1 && num_splits <= 256 && (long long)num_splits * head_groups * B > fa::kMaxGridX)
+        return fail(FA_ERR_UNSUPPORTED, "%s: num_splits * B * head groups = %lld chunks exceed %lld", name,
+                    (long long)num_splits * head_groups * B, fa::kMaxGridX);
     if (!seq_lens)
         return fail(FA_ERR_INVALID_ARGUMENT, "null seq_lens");
     if (!aligned(seq_lens, 4))
@@ -140,11 +154,11 @@ fa_status_t decode_common(const void* q, const void* k_cache, const void* v_cach
     if (need == 0 || workspace_bytes < need)
         return fail(FA_ERR_INVALID_ARGUMENT, "workspace too small: %zu bytes given, %zu needed",
                     workspace_bytes, need);
-    size_t rows = (size_t)B * (size_t)H * (size_t)num_splits;
-    size_t o_bytes = (rows * (size_t)d * sizeof(float) + 255) / 256 * 256;
+    char* ws = static_cast<char*>(workspace);
     fa::DecodeArgs a{q, k_cache, v_cache, seq_lens, o, lse,
-                     static_cast<float*>(workspace),
-                     reinterpret_cast<float*>(static_cast<char*>(workspace) + o_bytes),
+                     reinterpret_cast<float*>(ws + kQueueBytes),
+                     reinterpret_cast<float*>(ws + workspace_lse_offset(B, H, d, num_splits)),
+                     reinterpret_cast<unsigned long long*>(ws),
                      B, H, H_kv, N_max, d, num_splits, scale, window,
                      block_table, max_blocks, page_size, num_pages, kv_fp8, k_scale, v_scale};
     char what[64];

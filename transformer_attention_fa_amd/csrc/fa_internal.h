@@ -43,6 +43,7 @@ struct DecodeArgs {
     float* lse;          // [B,H] or nullptr
     float* part_o;       // [B,H,S,d]  workspace
     float* part_lse;     // [B,H,S]    workspace
+    unsigned long long* queue;   // chunk queue word, workspace
     int B, H, H_kv, N_max, d, num_splits;
     float scale;
     int window;          // the query sees the last `window` rows, 0 = all
