@@ -215,6 +215,31 @@ __device__ __forceinline__ int lds_read_int(const int* p)
     return v;
 }
 
+// LDS traffic of the cross-wave merge, which runs while the next chunk's
+// global->LDS loads are in flight: plain accesses would make the compiler wait
+// for those loads first.  Reads wait for their own results in the same block.
+__device__ __forceinline__ void lds_read_f32_4(float (&a)[4], const unsigned (&p)[4])
+{
+    asm volatile("ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_b32 %2, %6\n\tds_read_b32 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+                 : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+                 : "memory");
+}
+__device__ __forceinline__ void lds_read_f32x4_4(f32x4 (&a)[4], const unsigned (&p)[4])
+{
+    asm volatile("ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\tds_read_b128 %3, %7\n\t"
+                 "s_waitcnt lgkmcnt(0)"
+                 : "=&v"(a[0]), "=&v"(a[1]), "=&v"(a[2]), "=&v"(a[3])
+                 : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3])
+                 : "memory");
+}
+// a 16-byte LDS write; the barrier that follows waits for it
+__device__ __forceinline__ void lds_write_f32x4(unsigned p, f32x4 v)
+{
+    asm volatile("ds_write_b128 %0, %1" : : "v"(p), "v"(v) : "memory");
+}
+
 // s_waitcnt with vmcnt = n and the other counters left alone (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt()
@@ -421,8 +446,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     static_assert(kDecodeHeadGroup == 16, "a workgroup serves up to 16 query heads (the 16x16 MFMA columns)");
 
     constexpr int QB = 16 * 256;             // Q rows of the head group (16 x 256 B at most)
-    __shared__ __attribute__((aligned(1024))) char lds[NW * WAVE_LDS + QB];
-
+    constexpr int MH = 4;                    // heads per round of the cross-wave merge
+    constexpr int MB = NW * MH * D * 4;      // merge area: fp32 rows of MH heads from each wave
+    // the tile stages, the Q block and the merge area are disjoint, so the next
+    // chunk's Q block and first tiles can load while this chunk's merge runs
+    __shared__ __attribute__((aligned(1024))) char lds[NW * WAVE_LDS + QB + MB];
+    __shared__ float sh_m[NW * 16], sh_l[NW * 16];   // each wave's running max and sum per head
     __shared__ int next_item;
 
     const int tid = threadIdx.x;
@@ -434,108 +463,123 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     const int rank = lane_rank(p, lane_len);
     const int gy = p.H_kv * p.ngrp;          // head groups per sequence
 
-    for (int item = blockIdx.x; item < p.items;) {
+    char* const wl = lds + w * WAVE_LDS;
+    char* const qs = lds + NW * WAVE_LDS;
+    float* const sh_o = reinterpret_cast<float*>(lds + NW * WAVE_LDS + QB);
+    const unsigned wl_addr = (unsigned)(uintptr_t)(LDS_AS char*)wl;
+
+    // per-lane offsets of the tile loads inside a stage
+    int ld_k[LOADS], ld_v[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int pos = i * 64 + lane;
+        const int r = pos / CPR, cp = pos % CPR;
+        ld_k[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : kswz<D>(r, cp)) * 16;
+        ld_v[i] = r * ROWB + (KV8 ? vswz8<D>(r, cp) : dswz<D>(r, cp)) * 16;
+    }
+    // per-lane LDS read offsets inside a stage
+    int k_off[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (KV8)     // 8 bytes: d = 32*ks + 8*g4 .. +8 = half (g4 & 1) of chunk 2*ks + g4/2
+            k_off[ks] = l16 * ROWB + fswz<D>(l16, 2 * ks + (g4 >> 1)) * 16 + (g4 & 1) * 8;
+        else
+            k_off[ks] = l16 * ROWB + kswz<D>(l16, 4 * ks + g4) * 16;
+    }
+    // V^T fragments through transposing reads.  bf16: rows 4*g4 + l16/4 of
+    // the tile, two adjacent chunks of d block dm.  FP8 (32-key tiles): lane
+    // 16g + 2k + h reads 8 codes of row r_k (r_k = 4g + k for k < 4, 16 + 4g
+    // + k - 4 after), d = 16*dm + 8h .. +8; lane 16g + i then holds the codes
+    // of d = 16*dm + i for keys r_0..r_7, which are the keys this lane holds
+    // in P (4g..4g+3 of the first 16-key block of scores, 4g..4g+3 of the
+    // second)
+    int v_off[DB];
+    if constexpr (KV8) {
+        const int kk = (lane & 15) >> 1;
+        const int r = kk < 4 ? 4 * g4 + kk : 16 + 4 * g4 + (kk - 4);
+#pragma unroll
+        for (int dm = 0; dm < DB; ++dm) v_off[dm] = TILEB + r * ROWB + vswz8<D>(r, dm) * 16 + (lane & 1) * 8;
+    } else {
+        const int r = 4 * g4 + (l16 >> 2);
+#pragma unroll
+        for (int dm = 0; dm < DB; ++dm)
+            v_off[dm] = TILEB + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 + (l16 & 1) * 8;
+    }
+
+    // A chunk: the keys [j0, j0 + nkeys) of sequence b for the nh query heads
+    // from h0 that share KV head g; this wave streams its tiles w, w+4, ...
+    struct Chunk {
+        int g, b, h0, nh, j0, nkeys, nt_w;
+        const char* kbase;
+        const char* vbase;
+    };
+    auto describe = [&](int item) __attribute__((always_inline)) {
+        Chunk ch;
         const int c = item % p.S;
         const int y = (item / p.S) % gy;
-        const int g = y / p.ngrp;
         const int hg = y % p.ngrp;
-        const int b = sequence_of_rank(p, rank, item / (p.S * gy));
-        const int h0 = g * p.rep + hg * 16;      // first query head of the group
-        const int nh = min(16, p.rep - hg * 16); // heads in the group
-
-        const int len = p.B <= 64 ? __builtin_amdgcn_readlane(lane_len, b) : clamped_len(p, b);
+        ch.g = y / p.ngrp;
+        ch.b = sequence_of_rank(p, rank, item / (p.S * gy));
+        ch.h0 = ch.g * p.rep + hg * 16;          // first query head of the group
+        ch.nh = min(16, p.rep - hg * 16);        // heads in the group
+        const int len = p.B <= 64 ? __builtin_amdgcn_readlane(lane_len, ch.b) : clamped_len(p, ch.b);
         const int kfirst = key_start(p, len);
         int L = (len - kfirst + p.S - 1) / p.S;
         if (PAGED) L = (L + TK - 1) / TK * TK;   // chunks and tiles start on page-aligned rows
-        const int j0 = kfirst + c * L;
-        const int nkeys = max(0, min(j0 + L, len) - j0);
-        const int ntiles = (nkeys + TK - 1) / TK;
-        const int nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;   // tiles w, w+4, ...
-
-        const size_t kv_row0 = PAGED ? 0 : ((size_t)b * p.H_kv + g) * (size_t)p.N_max + (size_t)j0;
-        const char* kbase = p.k + kv_row0 * ROWB;
-        const char* vbase = p.v + kv_row0 * ROWB;
-        char* wl = lds + w * WAVE_LDS;
-
-        int ld_k[LOADS], ld_v[LOADS];
-    #pragma unroll
+        ch.j0 = kfirst + c * L;
+        ch.nkeys = max(0, min(ch.j0 + L, len) - ch.j0);
+        const int ntiles = (ch.nkeys + TK - 1) / TK;
+        ch.nt_w = ntiles > w ? (ntiles - w + NW - 1) / NW : 0;
+        const size_t kv_row0 = PAGED ? 0 : ((size_t)ch.b * p.H_kv + ch.g) * (size_t)p.N_max + (size_t)ch.j0;
+        ch.kbase = p.k + kv_row0 * ROWB;
+        ch.vbase = p.v + kv_row0 * ROWB;
+        return ch;
+    };
+    // tile t of chunk ch into stage s: rows past the chunk read as 0
+    auto issue = [&](const Chunk& ch, int t, int s) __attribute__((always_inline)) {
+        const int key0 = t * TK;
+        const unsigned bytes = (unsigned)min(TK, ch.nkeys - key0) * ROWB;
+        size_t off = (size_t)key0 * ROWB;
+        if constexpr (PAGED) {
+            // the tile's 16 rows lie in one page (page_size % 16 == 0, aligned chunks)
+            const int row = ch.j0 + key0;
+            const int blk = row / p.page_size;
+            int page = p.block_table[(size_t)ch.b * p.max_blocks + blk];
+            page = min(max(page, 0), p.num_pages - 1);           // never outside the pool
+            off = (((size_t)page * p.H_kv + ch.g) * p.page_size + (row - blk * p.page_size)) * ROWB;
+        }
+        const i32x4 rk = make_rsrc(ch.kbase + off, bytes);
+        const i32x4 rv = make_rsrc(ch.vbase + off, bytes);
+        char* dst = wl + s * 2 * TILEB;
+#pragma unroll
         for (int i = 0; i < LOADS; ++i) {
-            const int pos = i * 64 + lane;
-            const int r = pos / CPR, cp = pos % CPR;
-            ld_k[i] = r * ROWB + (KV8 ? fswz<D>(r, cp) : kswz<D>(r, cp)) * 16;
-            ld_v[i] = r * ROWB + (KV8 ? vswz8<D>(r, cp) : dswz<D>(r, cp)) * 16;
+            fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_k[i], 0, 0, kStreamPolicy);
+            fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_v[i], 0, 0, kStreamPolicy);
         }
-        // tile t of the chunk into stage s: rows past the chunk read as 0
-        auto issue = [&](int t, int s) __attribute__((always_inline)) {
-            const int key0 = t * TK;
-            const unsigned bytes = (unsigned)min(TK, nkeys - key0) * ROWB;
-            size_t off = (size_t)key0 * ROWB;
-            if constexpr (PAGED) {
-                // the tile's 16 rows lie in one page (page_size % 16 == 0, aligned chunks)
-                const int row = j0 + key0;
-                const int blk = row / p.page_size;
-                int page = p.block_table[(size_t)b * p.max_blocks + blk];
-                page = min(max(page, 0), p.num_pages - 1);           // never outside the pool
-                off = (((size_t)page * p.H_kv + g) * p.page_size + (row - blk * p.page_size)) * ROWB;
-            }
-            const i32x4 rk = make_rsrc(kbase + off, bytes);
-            const i32x4 rv = make_rsrc(vbase + off, bytes);
-            char* dst = wl + s * 2 * TILEB;
-    #pragma unroll
-            for (int i = 0; i < LOADS; ++i) {
-                fa_dec_buffer_load_lds(rk, (LDS_AS void*)(dst + i * 1024), 16, ld_k[i], 0, 0, kStreamPolicy);
-                fa_dec_buffer_load_lds(rv, (LDS_AS void*)(dst + TILEB + i * 1024), 16, ld_v[i], 0, 0, kStreamPolicy);
-            }
-        };
+    };
+    // A chunk's loads: this wave's 1 KB slice of the group's Q rows into the
+    // Q block (rows past the group read as 0; 16-byte chunks placed like a K
+    // tile row, whose fragment reads they repeat), then its first two tiles.
+    auto start_loads = [&](const Chunk& ch) __attribute__((always_inline)) {
+        const int pos = w * 64 + lane;                  // 16-byte chunk position in the Q block
+        const int qr = pos / (QROWB / 16), qc = pos % (QROWB / 16);
+        const i32x4 rq = make_rsrc(p.q + ((size_t)ch.b * p.H + ch.h0) * D, (unsigned)ch.nh * QROWB);
+        fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, qr * QROWB + kswz<D>(qr, qc) * 16, 0, 0, 0);
+        if (ch.nt_w > 0) issue(ch, w, 0);
+        if (ch.nt_w > 1) issue(ch, w + NW, 1);
+    };
 
-        // per-lane LDS read offsets inside a stage
-        int k_off[KS];
-    #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if constexpr (KV8)     // 8 bytes: d = 32*ks + 8*g4 .. +8 = half (g4 & 1) of chunk 2*ks + g4/2
-                k_off[ks] = l16 * ROWB + fswz<D>(l16, 2 * ks + (g4 >> 1)) * 16 + (g4 & 1) * 8;
-            else
-                k_off[ks] = l16 * ROWB + kswz<D>(l16, 4 * ks + g4) * 16;
-        }
-        // V^T fragments through transposing reads.  bf16: rows 4*g4 + l16/4 of
-        // the tile, two adjacent chunks of d block dm.  FP8 (32-key tiles): lane
-        // 16g + 2k + h reads 8 codes of row r_k (r_k = 4g + k for k < 4, 16 + 4g
-        // + k - 4 after), d = 16*dm + 8h .. +8; lane 16g + i then holds the codes
-        // of d = 16*dm + i for keys r_0..r_7, which are the keys this lane holds
-        // in P (4g..4g+3 of the first 16-key block of scores, 4g..4g+3 of the
-        // second)
-        int v_off[DB];
-        if constexpr (KV8) {
-            const int kk = (lane & 15) >> 1;
-            const int r = kk < 4 ? 4 * g4 + kk : 16 + 4 * g4 + (kk - 4);
-    #pragma unroll
-            for (int dm = 0; dm < DB; ++dm) v_off[dm] = TILEB + r * ROWB + vswz8<D>(r, dm) * 16 + (lane & 1) * 8;
-        } else {
-            const int r = 4 * g4 + (l16 >> 2);
-    #pragma unroll
-            for (int dm = 0; dm < DB; ++dm)
-                v_off[dm] = TILEB + r * QROWB + dswz<D>(r, 2 * dm + ((l16 & 3) >> 1)) * 16 + (l16 & 1) * 8;
-        }
-
-        f32x4 oacc[DB];
-    #pragma unroll
-        for (int i = 0; i < DB; ++i) oacc[i] = f32x4{};
-        float m_run = kNegInf, nbase = 0.f, l_run = 0.f;
-
-        // ---- Q rows of the group into LDS (one 1 KB slice per wave; rows past the
-        // group read as 0; 16-byte chunks placed like a K tile row, whose fragment
-        // reads they repeat), then the first two tiles of this wave
-        char* qs = lds + NW * WAVE_LDS;
-        {
-            const int pos = w * 64 + lane;                  // 16-byte chunk position in the Q block
-            const int qr = pos / (QROWB / 16), qc = pos % (QROWB / 16);
-            const i32x4 rq = make_rsrc(p.q + ((size_t)b * p.H + h0) * D, (unsigned)nh * QROWB);
-            fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, qr * QROWB + kswz<D>(qr, qc) * 16, 0, 0, 0);
-        }
-        if (nt_w > 0) issue(w, 0);
-        if (nt_w > 1) issue(w + NW, 1);
-        if (nt_w > 1) wait_vmcnt<4 * LOADS>();      // the Q slice (older than both tiles) landed
-        else if (nt_w > 0) wait_vmcnt<2 * LOADS>();
+    int item = blockIdx.x;                   // < p.items: the grid is never larger
+    Chunk cur = describe(item);
+    start_loads(cur);
+    bool prefetched = false;                 // cur's loads were issued during the previous chunk's merge
+    for (;;) {
+        // this wave's Q slice has landed (then the block, after the barrier).
+        // Loads issued in one go land in order: the tiles may still fly.  After
+        // a prefetch the previous chunk's partial stores follow them: wait for all.
+        if (prefetched) wait_vmcnt<0>();
+        else if (cur.nt_w > 1) wait_vmcnt<4 * LOADS>();
+        else if (cur.nt_w > 0) wait_vmcnt<2 * LOADS>();
         else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();               // every wave waited for its own slice
         // Q^T fragments (B of S^T): head l16, d = 32*ks + 8*g4 .. +8 (chunk 4*ks + g4)
@@ -548,7 +592,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
             else lds_read_k2(qf, qa + kswz<D>(l16, g4) * 16, qa + kswz<D>(l16, 4 + g4) * 16);
         }
 
-        const unsigned wl_addr = (unsigned)(uintptr_t)(LDS_AS char*)wl;
+        f32x4 oacc[DB];
+#pragma unroll
+        for (int i = 0; i < DB; ++i) oacc[i] = f32x4{};
+        float m_run = kNegInf, nbase = 0.f, l_run = 0.f;
+
         // online softmax of a lane's scores; returns their weights
         auto online = [&](auto& sc) __attribute__((always_inline)) {
             constexpr int N = sizeof(sc) / sizeof(float);
@@ -560,7 +608,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
                 const float m_new = fmaxf(m_run, m_blk);
                 const float alpha = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
                 l_run *= alpha;
-    #pragma unroll
+#pragma unroll
                 for (int dm = 0; dm < DB; ++dm) oacc[dm] *= alpha;
                 m_run = m_new;
                 nbase = (m_new == kNegInf) ? 0.f : -m_new;
@@ -572,22 +620,22 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
                 // S^T of the two 16-key blocks of the tile; K codes -> bf16 (exact)
                 constexpr int NK = 2 * KS;
                 unsigned ka[NK];
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < KS; ++ks) ka[kb * KS + ks] = st + k_off[ks] + kb * 16 * ROWB;
                 u32x2 k8[NK];
                 if constexpr (NK == 8) lds_read_b64x8(k8, ka);
                 else lds_read_b64n<4>(k8, ka);
                 unsigned vaddr[DB];
-    #pragma unroll
+#pragma unroll
                 for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
                 u32x2 v8[DB];
                 lds_read_tr8<DB>(v8, vaddr);
                 f32x4 sc2[2] = {f32x4{}, f32x4{}};
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
-    #pragma unroll
+#pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
                         const u32x2 w8 = k8[kb * KS + ks];
                         const unsigned long long lo = e4m3x4_to_bf16x4(w8[0]), hi = e4m3x4_to_bf16x4(w8[1]);
@@ -597,19 +645,19 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
                     }
                 // keys past the chunk end: key 16*kb + 4*g4 + r of the tile
                 float sc[8];
-    #pragma unroll
+#pragma unroll
                 for (int kb = 0; kb < 2; ++kb) {
-                    const int lim = nkeys - t * TK - 16 * kb - 4 * g4;
-    #pragma unroll
+                    const int lim = cur.nkeys - t * TK - 16 * kb - 4 * g4;
+#pragma unroll
                     for (int r = 0; r < 4; ++r) sc[4 * kb + r] = (r < lim) ? sc2[kb][r] : kNegInf;
                 }
                 online(sc);
                 float e[8];
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 8; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
                 l_run += ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
                 const bf16x8 pf = __builtin_convertvector((f32x8{e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]}), bf16x8);
-    #pragma unroll
+#pragma unroll
                 for (int dm = 0; dm < DB; ++dm) {
                     const unsigned long long lo = e4m3x4_to_bf16x4(v8[dm][0]), hi = e4m3x4_to_bf16x4(v8[dm][1]);
                     const bf16x8 vf = __builtin_bit_cast(bf16x8, (u32x4{(unsigned)lo, (unsigned)(lo >> 32), (unsigned)hi,
@@ -621,25 +669,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
                 if constexpr (KS == 4) lds_read_k4(kf, st + k_off[0], st + k_off[1], st + k_off[2], st + k_off[3]);
                 else lds_read_k2(kf, st + k_off[0], st + k_off[1]);
                 f32x4 sc = {};
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < KS; ++ks) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[ks], qf[ks], sc, 0, 0, 0);
                 unsigned vaddr[DB];
-    #pragma unroll
+#pragma unroll
                 for (int dm = 0; dm < DB; ++dm) vaddr[dm] = st + v_off[dm];
                 i16x4 vf[DB];
                 if constexpr (DB == 8) lds_read_vt8(vf, vaddr);
                 else lds_read_vt4(vf, vaddr);
                 // keys past the chunk end
-                const int lim = nkeys - t * TK - 4 * g4;
-    #pragma unroll
+                const int lim = cur.nkeys - t * TK - 4 * g4;
+#pragma unroll
                 for (int r = 0; r < 4; ++r) sc[r] = (r < lim) ? sc[r] : kNegInf;
                 online(sc);
                 f32x4 e;
-    #pragma unroll
+#pragma unroll
                 for (int r = 0; r < 4; ++r) e[r] = fast_exp2(__builtin_fmaf(sc[r], p.c, nbase));
                 l_run += (e[0] + e[1]) + (e[2] + e[3]);
                 const bf16x4 pf = __builtin_convertvector(e, bf16x4);
-    #pragma unroll
+#pragma unroll
                 for (int dm = 0; dm < DB; ++dm)
                     oacc[dm] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4, vf[dm]), pf, oacc[dm], 0, 0, 0);
             }
@@ -651,6 +699,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         // other workgroups for long, early enough that the atomic's round trip
         // overlaps the last tile.  The wait for the tile before the last
         // allows for it (one more operation in flight).
+        const int nt_w = cur.nt_w;
         const bool claiming = p.queue && w == 0;
         unsigned long long claim = 0;
         for (int i = 0; i < nt_w; ++i) {
@@ -661,84 +710,116 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
                 wait_vmcnt<0>();
             }
             compute(w + i * NW, i & 1);
-            if (i + 2 < nt_w) issue(w + (i + 2) * NW, i & 1);   // this stage's reads are complete
+            if (i + 2 < nt_w) issue(cur, w + (i + 2) * NW, i & 1);   // this stage's reads are complete
             if (claiming && i + 3 == nt_w && lane == 0) claim = atomicAdd(p.queue, 1ull);
         }
         if (claiming && nt_w < 3 && lane == 0) claim = atomicAdd(p.queue, 1ull);
 
-        // ---- merge the 4 waves through LDS and write the chunk's partial result
+        // ---- merge the 4 waves through the merge area and write the chunk's
+        // partial result, in rounds of MH heads.  Row (w, head h - MH*r) holds
+        // the 4 accumulator values of d-block dm as 16-byte chunk 4*dm + g4,
+        // with the d-block XORed with the head so the MH heads of one write
+        // cover all banks.
         const float l_head = swap16_sum(swap32_sum(l_run));      // sum over the 4 key groups
-        lds_barrier();                                            // tile slices are free
-        float* sh_m = reinterpret_cast<float*>(lds);             // [NW][16]
-        float* sh_l = sh_m + NW * 16;                             // [NW][16]
-        float* sh_o = sh_l + NW * 16;                             // [NW][16][D]
         if (g4 == 0) {
             sh_m[w * 16 + l16] = m_run;
             sh_l[w * 16 + l16] = l_head;
         }
-        // row (w, head l16): the 4 accumulator values of d-block dm are 16
-        // contiguous bytes, chunk 4*dm + g4 of the row; the chunk index is XORed
-        // with the head so the 16 heads of one write land in different banks
-    #pragma unroll
-        for (int dm = 0; dm < DB; ++dm)
-            *reinterpret_cast<f32x4*>(sh_o + (w * 16 + l16) * D + (((4 * dm + g4) ^ l16) << 2)) = oacc[dm];
-        lds_barrier();
-        // thread (head hh = tid/16, part q = tid%16): the 4-float chunks q and
-        // q+16 of the head's row (q alone at d = 64).  The head's 4 wave weights
-        // are computed once per thread, each chunk is one 16-byte read per wave
-        // (chunk positions q ^ hh: the 16 parts of a head cover all banks), and
-        // the 16 parts of a head store whole runs of the row.
-        constexpr int CH = D / 64;               // chunks per thread
-        const int hh = tid >> 4, q = tid & 15;
-        if (hh < nh) {
-            float mw[NW], mm = kNegInf;
-    #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                mw[ww] = sh_m[ww * 16 + hh];
-                mm = fmaxf(mm, mw[ww]);
+        const unsigned o_addr = (unsigned)(uintptr_t)(LDS_AS float*)sh_o;
+        auto put_rows = [&](int r) __attribute__((always_inline)) {
+            const int hl = l16 - MH * r;
+            if (hl >= 0 && hl < MH) {
+#pragma unroll
+                for (int dm = 0; dm < DB; ++dm)
+                    lds_write_f32x4(o_addr + ((w * MH + hl) * D + ((4 * (dm ^ hl) + g4) << 2)) * 4, oacc[dm]);
             }
-            const float base = (mm == kNegInf) ? 0.f : mm;
-            float a[NW], ll = 0.f;
-    #pragma unroll
-            for (int ww = 0; ww < NW; ++ww) {
-                a[ww] = (mw[ww] == kNegInf) ? 0.f : fast_exp2(mw[ww] - base);
-                ll += a[ww] * sh_l[ww * 16 + hh];
-            }
-            const float scale_out = ll > 0.f ? p.v_scale / ll : 0.f;
-            const size_t row = ((size_t)b * p.H + h0 + hh) * p.S + c;
-    #pragma unroll
-            for (int k = 0; k < CH; ++k) {
-                const int c4 = q + 16 * k;       // chunk of the row: d = 4*c4 .. 4*c4+3
-                f32x4 oo = {};
-    #pragma unroll
-                for (int ww = 0; ww < NW; ++ww)
-                    oo += a[ww] * *reinterpret_cast<const f32x4*>(sh_o + (ww * 16 + hh) * D + ((c4 ^ hh) << 2));
-                const f32x4 val = oo * scale_out;
-                if (p.o) {
-                    // S == 1 (row indexes (b, h)): the merge of one chunk has weight
-                    // exactly 1, so this is the value it would write
-                    *reinterpret_cast<bf16x4*>(p.o + row * D + 4 * c4) = __builtin_convertvector(val, bf16x4);
-                } else {
-                    *reinterpret_cast<f32x4*>(p.part_o + row * D + 4 * c4) = val;
-                }
-            }
-            if (q == 0) {
-                const float lse_c = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
-                if (p.o) {
-                    if (p.lse) p.lse[row] = lse_c;
-                } else {
-                    p.part_lse[row] = lse_c;
-                }
-            }
-        }
+        };
+        put_rows(0);
         if (tid == 0)
             next_item = p.queue ? (int)min((long long)p.grid + settle_claim(p.queue, claim), (long long)p.items)
                                 : p.items;
-        lds_barrier();               // the tile slices, the Q block and the merge area are free again
-        item = __builtin_amdgcn_readfirstlane(lds_read_int(&next_item));
+        lds_barrier();               // every wave's tiles are done and its round-0 rows written
+        const int nxt = __builtin_amdgcn_readfirstlane(lds_read_int(&next_item));
+        // The next chunk's Q block and first tiles load while this merge runs:
+        // every wave has read this chunk's Q fragments and finished its tiles.
+        Chunk nch;
+        if (nxt < p.items) {
+            nch = describe(nxt);
+            start_loads(nch);
+        }
+        const int rounds = (cur.nh + MH - 1) / MH;
+        for (int r = 0; r < rounds; ++r) {
+            if (r > 0) {
+                lds_barrier();       // the previous round's rows are read
+                put_rows(r);
+                lds_barrier();
+            }
+            // wave 0, thread (head h = MH*r + tid/16, part q = tid%16): the
+            // 4-float chunks q and q+16 of the head's row (q alone at d = 64).
+            // The head's 4 wave weights are computed once per thread, each
+            // chunk is one 16-byte read per wave, and the 16 parts of a head
+            // store whole runs of the row.
+            constexpr int CH = D / 64;               // chunks per thread
+            const int hl = tid >> 4, q = tid & 15, hh = MH * r + hl;
+            if (tid < 16 * MH && hh < cur.nh) {
+                static_assert(NW == 4, "the merge reads one value per wave, four at a time");
+                float mw[NW], lw[NW], mm = kNegInf;
+                {
+                    const unsigned ma = (unsigned)(uintptr_t)(LDS_AS float*)sh_m + hh * 4;
+                    const unsigned la = (unsigned)(uintptr_t)(LDS_AS float*)sh_l + hh * 4;
+                    const unsigned pm[NW] = {ma, ma + 64, ma + 128, ma + 192};
+                    const unsigned pl[NW] = {la, la + 64, la + 128, la + 192};
+                    lds_read_f32_4(mw, pm);
+                    lds_read_f32_4(lw, pl);
+                }
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) mm = fmaxf(mm, mw[ww]);
+                const float base = (mm == kNegInf) ? 0.f : mm;
+                float a[NW], ll = 0.f;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) {
+                    a[ww] = (mw[ww] == kNegInf) ? 0.f : fast_exp2(mw[ww] - base);
+                    ll += a[ww] * lw[ww];
+                }
+                const float scale_out = ll > 0.f ? p.v_scale / ll : 0.f;
+                const size_t row = ((size_t)cur.b * p.H + cur.h0 + hh) * p.S + (size_t)(item % p.S);
+#pragma unroll
+                for (int k = 0; k < CH; ++k) {
+                    const int c4 = q + 16 * k;       // chunk of the row: d = 4*c4 .. 4*c4+3
+                    f32x4 ow[NW];
+                    {
+                        const unsigned oa = o_addr + ((hl * D) + ((c4 ^ (hl << 2)) << 2)) * 4;
+                        const unsigned po[NW] = {oa, oa + MH * D * 4, oa + 2 * MH * D * 4, oa + 3 * MH * D * 4};
+                        lds_read_f32x4_4(ow, po);
+                    }
+                    f32x4 oo = {};
+#pragma unroll
+                    for (int ww = 0; ww < NW; ++ww) oo += a[ww] * ow[ww];
+                    const f32x4 val = oo * scale_out;
+                    if (p.o) {
+                        // S == 1 (row indexes (b, h)): the merge of one chunk has weight
+                        // exactly 1, so this is the value it would write
+                        *reinterpret_cast<bf16x4*>(p.o + row * D + 4 * c4) = __builtin_convertvector(val, bf16x4);
+                    } else {
+                        *reinterpret_cast<f32x4*>(p.part_o + row * D + 4 * c4) = val;
+                    }
+                }
+                if (q == 0) {
+                    const float lse_c = ll > 0.f ? (mm + __builtin_log2f(ll)) * kLn2 : kNegInf;
+                    if (p.o) {
+                        if (p.lse) p.lse[row] = lse_c;
+                    } else {
+                        p.part_lse[row] = lse_c;
+                    }
+                }
+            }
+        }
+        if (nxt >= p.items) break;
+        item = nxt;
+        cur = nch;
+        prefetched = true;
     }
 }
-
 
 struct CombineParams {
     const float* part_o;
