@@ -905,6 +905,56 @@ def test_decode_chunk_queue_graph_replays_match_eager():
         torch.cuda.synchronize()
 
 
+# Each kernel variant with more chunks than the device holds at once (512
+# workgroups at d = 128, 768 at d = 64 on 256 CUs), so the queue runs in all of
+# them: more than 64 sequences (index order, lengths read per chunk), d = 64,
+# a sliding window, the FP8 and the paged cache.
+QUEUE_CASES = [
+    # name, B, H, H_kv, d, N_max, splits, kind
+    ("bf16_B80", 80, 8, 2, 128, 300, 8, "bf16"),
+    ("bf16_d64", 16, 16, 4, 64, 500, 16, "bf16"),
+    ("window_d128", 16, 8, 4, 128, 600, 16, "window"),
+    ("fp8_d64", 16, 16, 4, 64, 600, 16, "fp8"),
+    ("fp8_B70", 70, 4, 2, 128, 256, 4, "fp8"),
+    ("paged_d64", 16, 16, 4, 64, 512, 16, "paged"),
+]
+
+
+@pytest.mark.parametrize("case", QUEUE_CASES, ids=lambda c: c[0])
+def test_decode_chunk_queue_kernel_variants(case):
+    import torch
+    name, B, H, H_kv, d, N_max, S, kind = case
+    assert B * H_kv * S > (512 if d == 128 else 768)
+    rng = np.random.default_rng(B * 1000 + d)
+    lens = rng.integers(1, N_max + 1, B).astype(np.int32)
+    lens[:3] = [1, 17, N_max]
+    say(f"decode chunk queue variant {name}")
+    if kind == "fp8":
+        k_scale, v_scale = 0.011, 2.0 ** -5
+        fspec = inputs.Decode(f"queue_{name}", B, H, H_kv, d, 1, N_max, N_max, S, 97, dtype="e4m3",
+                              k_scale=k_scale, v_scale=v_scale)
+        fdata = inputs.decode_inputs_fp8(fspec, seq_lens=lens)
+        o, lse = _fp8_run(fdata, S, k_scale, v_scale)
+        o_ref, lse_ref = oracle.decode_fp8(fdata.q, fdata.k_cache, fdata.v_cache, k_scale, v_scale, lens,
+                                           fspec.scale)
+    else:
+        spec = inputs.Decode(f"queue_{name}", B, H, H_kv, d, 1, N_max, N_max, S, 97)
+        data = inputs.decode_inputs(spec, seq_lens=lens)
+        dl = torch.from_numpy(lens).cuda()
+        if kind == "paged":
+            kp, vp, table = _paged(data, 16, 101)
+            o, lse = api.decode_paged(bf16_to_device(data.q), bf16_to_device(kp), bf16_to_device(vp),
+                                      torch.from_numpy(table).cuda(), dl, num_splits=S, scale=spec.scale)
+            o_ref, lse_ref = oracle.decode_paged(data.q, kp, vp, np.maximum(table, 0), lens, spec.scale)
+        else:
+            window = 200 if kind == "window" else None
+            o, lse = api.decode(bf16_to_device(data.q), bf16_to_device(data.k_cache), bf16_to_device(data.v_cache),
+                                dl, num_splits=S, scale=spec.scale, window=window)
+            o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, lens, spec.scale, window=window)
+    torch.cuda.synchronize()
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=name)
+
+
 # ------------------------------------------------------------------ HIP graph capture
 def test_hip_graph_capture_replays_match_eager():
     """A prefill call and a decode step captured in one HIP graph (through
