@@ -19,10 +19,11 @@
 // resident set that takes chunks, longest sequence first, from a counter in
 // the workspace: the 8 XCDs stream at rates up to ~12 % apart, and chunks
 // dealt round robin (as the hardware deals workgroups) leave the fast XCDs
-// idle while the slow ones finish.  The chunk is cut into 16-key tiles (32 for FP8) dealt round robin
-// to the 4 waves; each wave streams its tiles into its own slice of LDS with
-// buffer_load_dwordx4 ... lds (two tiles in flight, no workgroup barrier) and
-// computes on the matrix cores:
+// idle while the slow ones finish.  The next chunk's first loads go out while
+// the current one's waves merge.  The chunk is cut into 16-key tiles (32 for
+// FP8) dealt round robin to the 4 waves; each wave streams its tiles into its
+// own slice of LDS with buffer_load_dwordx4 ... lds (two tiles in flight, no
+// workgroup barrier) and computes on the matrix cores:
 //   S^T (16 keys x 16 heads) = K Q^T     v_mfma_f32_16x16x32_bf16, K from LDS
 //   O^T (d x 16 heads)     += V^T P^T    v_mfma_f32_16x16x16_bf16, V^T from LDS
 //                                         through transposing reads
@@ -39,7 +40,8 @@
 // Padding heads (past the group) have zero queries and are discarded.  The
 // online softmax of "Attention variants" §3 runs per wave (running max raised
 // only when a tile max exceeds it by more than 8, so p <= 256); the 4 waves
-// are merged at the end with the same rescale rule and the chunk writes
+// are merged at the end (through an LDS area of their own, 4 heads a round)
+// with the same rescale rule and the chunk writes
 // o_c = O/l (fp32) and lse_c = m + ln l; an empty chunk writes lse_c = -inf,
 // o_c = 0.
 //
