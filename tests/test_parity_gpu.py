@@ -494,6 +494,25 @@ def test_decode_paged(page_size, num_splits):
             label=f"page {page_size} S={num_splits}")
 
 
+@pytest.mark.parametrize("d,page_size,num_splits", [(128, 16, 1), (128, 64, 2), (64, 32, 1)])
+def test_decode_paged_long_chunks(d, page_size, num_splits):
+    """Chunks of more than 64 tiles per wave (over 4096 keys): the kernel holds
+    the first 64 block-table entries of each wave in its lanes and reads the
+    later ones one by one."""
+    import torch
+    spec = _small_decode_spec(H=4, H_kv=1, d=d, N_max=9000, B=3, seed=53)
+    lens = np.array([4097, 9000, 6000], np.int32)
+    data = inputs.decode_inputs(spec, seq_lens=lens)
+    kp, vp, table = _paged(data, page_size, 59)
+    o, lse = api.decode_paged(bf16_to_device(data.q), bf16_to_device(kp), bf16_to_device(vp),
+                              torch.from_numpy(table).cuda(), torch.from_numpy(lens).cuda(), num_splits=num_splits,
+                              scale=spec.scale)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.decode(data.q, data.k_cache, data.v_cache, lens, spec.scale)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL,
+            label=f"paged long d{d} p{page_size} S={num_splits}")
+
+
 def test_decode_paged_d64_mqa():
     import torch
     spec = _small_decode_spec(H=16, H_kv=1, d=64, N_max=900, B=3, seed=43)

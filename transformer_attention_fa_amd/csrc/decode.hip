@@ -512,8 +512,14 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
     // from h0 that share KV head g; this wave streams its tiles w, w+4, ...
     struct Chunk {
         int g, b, h0, nh, j0, nkeys, nt_w;
+        int pages;                  // paged cache: lane l holds the page of this wave's tile l
         const char* kbase;
         const char* vbase;
+    };
+    // paged cache: the block-table entry of tile t of chunk ch, clamped into the pool
+    auto table_page = [&](const Chunk& ch, int t) __attribute__((always_inline)) {
+        const int page = p.block_table[(size_t)ch.b * p.max_blocks + (ch.j0 + t * TK) / p.page_size];
+        return min(max(page, 0), p.num_pages - 1);           // never outside the pool
     };
     auto describe = [&](int item) __attribute__((always_inline)) {
         Chunk ch;
@@ -535,20 +541,25 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         const size_t kv_row0 = PAGED ? 0 : ((size_t)ch.b * p.H_kv + ch.g) * (size_t)p.N_max + (size_t)ch.j0;
         ch.kbase = p.k + kv_row0 * ROWB;
         ch.vbase = p.v + kv_row0 * ROWB;
+        // One block-table read per lane and chunk: the entry of this wave's
+        // tile `lane`.  Read per tile instead, the entry would be a vector
+        // load whose use waits for every tile load in flight before it.
+        ch.pages = 0;
+        if (PAGED && lane < ch.nt_w) ch.pages = table_page(ch, w + lane * NW);
         return ch;
     };
-    // tile t of chunk ch into stage s: rows past the chunk read as 0
-    auto issue = [&](const Chunk& ch, int t, int s) __attribute__((always_inline)) {
+    // this wave's tile i of chunk ch into stage s: rows past the chunk read as 0
+    auto issue = [&](const Chunk& ch, int i, int s) __attribute__((always_inline)) {
+        const int t = w + i * NW;
         const int key0 = t * TK;
         const unsigned bytes = (unsigned)min(TK, ch.nkeys - key0) * ROWB;
         size_t off = (size_t)key0 * ROWB;
         if constexpr (PAGED) {
             // the tile's 16 rows lie in one page (page_size % 16 == 0, aligned chunks)
             const int row = ch.j0 + key0;
-            const int blk = row / p.page_size;
-            int page = p.block_table[(size_t)ch.b * p.max_blocks + blk];
-            page = min(max(page, 0), p.num_pages - 1);           // never outside the pool
-            off = (((size_t)page * p.H_kv + ch.g) * p.page_size + (row - blk * p.page_size)) * ROWB;
+            const int page = i < 64 ? __builtin_amdgcn_readlane(ch.pages, i)
+                                    : __builtin_amdgcn_readfirstlane(table_page(ch, t));
+            off = (((size_t)page * p.H_kv + ch.g) * p.page_size + (row % p.page_size)) * ROWB;
         }
         const i32x4 rk = make_rsrc(ch.kbase + off, bytes);
         const i32x4 rv = make_rsrc(ch.vbase + off, bytes);
@@ -567,8 +578,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
         const int qr = pos / (QROWB / 16), qc = pos % (QROWB / 16);
         const i32x4 rq = make_rsrc(p.q + ((size_t)ch.b * p.H + ch.h0) * D, (unsigned)ch.nh * QROWB);
         fa_dec_buffer_load_lds(rq, (LDS_AS void*)(qs + w * 1024), 16, qr * QROWB + kswz<D>(qr, qc) * 16, 0, 0, 0);
-        if (ch.nt_w > 0) issue(ch, w, 0);
-        if (ch.nt_w > 1) issue(ch, w + NW, 1);
+        if (ch.nt_w > 0) issue(ch, 0, 0);
+        if (ch.nt_w > 1) issue(ch, 1, 1);
     };
 
     int item = blockIdx.x;                   // < p.items: the grid is never larger
@@ -712,7 +723,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(SplitParams p)
                 wait_vmcnt<0>();
             }
             compute(w + i * NW, i & 1);
-            if (i + 2 < nt_w) issue(cur, w + (i + 2) * NW, i & 1);   // this stage's reads are complete
+            if (i + 2 < nt_w) issue(cur, i + 2, i & 1);   // this stage's reads are complete
             if (claiming && i + 3 == nt_w && lane == 0) claim = atomicAdd(p.queue, 1ull);
         }
         if (claiming && nt_w < 3 && lane == 0) claim = atomicAdd(p.queue, 1ull);
