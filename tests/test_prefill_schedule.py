@@ -10,14 +10,18 @@ every tile a wave owns gets S, then its softmax, then PV, in the periods its
 role fixes; every LDS slot a period reads holds the tile it should, and no
 period loads into a slot it reads; the entered item's Q block is complete in
 the Q area when the switch period reads it, and no Q slice loads in a switch
-period; every item's rows are written once by every wave.  The model follows
-the kernel's code and must be kept in step with it.
+period; every item's rows are written once by every wave, and every 32-row
+group of every head's output by exactly one wave (causal launches with an even
+GQA ratio pair two heads per item: half the rows, waves 0-3 on the first head
+and waves 4-7 on the second).  The model follows the kernel's code and must be
+kept in step with it.
 """
 import random
 
 import pytest
 
 _FLIP = False  # plants a slot-parity mistake (test of the checker itself)
+_SAME_HEAD = False  # plants a paired-item mistake: waves 4-7 on the first head too
 
 BM, BN, NW = 256, 64, 8
 
@@ -28,20 +32,23 @@ def tdiv(a, b):  # C++ truncating division
 
 def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=256, max_groups=None):
     rep = H // Hkv
-    nqb = cdiv(Nq, BM)
-    items = nqb * H * B
+    pair = persist and causal and rep % 2 == 0
+    BMI = BM // 2 if pair else BM
+    hpb = H // 2 if pair else H
+    nqb = cdiv(Nq, BMI)
+    items = nqb * hpb * B
     if items == 0: return
     grid = items; xcd = 0
     if persist:
         grid = min(grid, resident)
         if cap > 0: grid = min(grid, cap)
-        if ((H * B) & 7) == 0 and grid >= 8:
+        if ((hpb * B) & 7) == 0 and grid >= 8:
             grid = grid // 8 * 8; xcd = 1
     off = Nk - Nq
     win = window if causal else 0
     QPARTS = 8
     def decompose(i):
-        HB = H * B; head0, nheads, slot = 0, HB, i
+        HB = hpb * B; head0, nheads, slot = 0, HB, i
         if (HB & 7) == 0:
             nheads = HB >> 3; head0 = (i & 7) * nheads; slot = i >> 3
         gsz = min(group, nheads)
@@ -49,17 +56,19 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
         g0 = grp * gsz; gcount = min(gsz, nheads - g0)
         j = rem // gcount; bh = head0 + g0 + rem % gcount
         qb = nqb - 1 - j if causal else j
-        return qb, bh % H, bh // H
+        return qb, bh % hpb, bh // hpb
     def item_at(i):
-        qb, h, b = decompose(i)
-        q0 = qb * BM
+        qb, hh, b = decompose(i)
+        h = 2 * hh if pair else hh
+        q0 = qb * BMI
         kend = Nk
-        if causal: kend = min(Nk, q0 + BM + off)
+        if causal: kend = min(Nk, q0 + BMI + off)
         nkb = cdiv(kend, BN) if kend > 0 else 0
         kb_lo = 0
         if causal and win > 0: kb_lo = min(nkb, max(0, q0 + off - win + 1) // BN)
         nkb = max(nkb, kb_lo + (2 if persist else 1))
-        return dict(bh=b * H + h, bg=b * Hkv + h // rep, q0=q0, nkb=nkb, kb_lo=kb_lo, id=i)
+        return dict(bh=b * H + h, bh2=b * H + h + (1 if pair and not _SAME_HEAD else 0), bg=b * Hkv + h // rep,
+                    q0=q0, nkb=nkb, kb_lo=kb_lo, id=i)
     def item_id(g, r):
         if not persist: return g if r == 0 else -1
         if xcd:
@@ -69,6 +78,7 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
         k = r * grid + ((grid - 1 - g) if (r & 1) else g)
         return k if k < items else -1
     covered = set()
+    rows_out = {}
     groups = range(grid) if max_groups is None else range(min(grid, max_groups))
     for g in groups:
         logs = {}
@@ -91,7 +101,7 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
                 ev.append(('loadV', 0, (cur['id'], cur['kb_lo']), cur['kb_lo'] & 1))
             for part in range(8): ev.append(('loadQ', 0, cur['id'], part))
             def geom(it):
-                qw0 = it['q0'] + wr * 32
+                qw0 = it['q0'] + ((w & 3) if pair else wr) * 32
                 nkb_w = it['nkb']
                 if causal: nkb_w = max(0, min(it['nkb'], tdiv(qw0 + 31 + off, BN) + 1))
                 windowed = causal and win > 0
@@ -111,7 +121,9 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
                 if has_cur:
                     qw0, nkb_w, a_w = geom(cur); wave_g = (qw0, nkb_w, a_w)
                     ev.append(('readQ', period, cur['id']))
-                if has_prev: ev.append(('out', period, prev['id']))
+                if has_prev:
+                    ev.append(('out', period, prev['id'], prev['bh2'] if pair and role == 1 else prev['bh'],
+                               geom(prev)[0]))
                 if not has_cur:
                     period += 1; break
                 do_s = nkb_w > a_w and a_w == cur['kb_lo']
@@ -233,10 +245,15 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
                 else: assert ps['SM'] == ps['S'] + 1 and ps['PV'] == ps['SM'], (g, w, key, lst)
             # the wave's tiles: exactly [a_w, nkb_w) of each item it runs
             outs = [e for e in logs[w][1] if e[0] == 'out']
-            for e in outs: covered.add((e[2], w))
+            for e in outs:
+                covered.add((e[2], w))
+                if e[4] < Nq: rows_out[(e[3], e[4])] = rows_out.get((e[3], e[4]), 0) + 1
     # every item's rows written once per wave
     if max_groups is None:
         assert len(covered) == items * NW, (len(covered), items * NW)
+        want = {(bh, q) for bh in range(B * H) for q in range(0, Nq, 32)}
+        assert set(rows_out) == want and all(c == 1 for c in rows_out.values()), \
+            ('output rows', sorted(set(rows_out) ^ want)[:8], [k for k, c in rows_out.items() if c != 1][:8])
 
 
 WORKLOADS = [(4, 64, 1, 4096, 4096, False, 0, 0), (8, 32, 32, 2048, 2048, True, 0, 0),
@@ -281,3 +298,15 @@ def test_model_catches_a_slot_parity_mistake(monkeypatch):
             run(2, 8, 2, 600, 600, True, 0, 3)
     finally:
         _FLIP = False
+
+
+def test_model_catches_a_paired_head_mistake():
+    """The output-row check is live: with both wave groups of a paired item on
+    the same head, one head's rows are written twice and the other's never."""
+    global _SAME_HEAD
+    _SAME_HEAD = True
+    try:
+        with pytest.raises(AssertionError):
+            run(1, 4, 2, 300, 300, True, 0, 2)
+    finally:
+        _SAME_HEAD = False

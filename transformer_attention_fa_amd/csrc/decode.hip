@@ -929,17 +929,17 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(CombineParams p)
 // Workgroups of a kernel that fit on the current device at once.  Cached per
 // device and kernel (host threads may race to fill an entry; they store the
 // same value); 0 if the runtime cannot say.
-template <typename K>
-int resident_blocks(K kernel, int threads)
+template <auto Kernel>
+int resident_blocks(int threads)
 {
-    static std::atomic<int> cache[64];
+    static std::atomic<int> cache[64];    // one per instantiation, i.e. per kernel
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     const int known = cache[dev].load(std::memory_order_relaxed);
     if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0) != hipSuccess) return 0;
     const int n = cus * (per_cu > 0 ? per_cu : 1);
     cache[dev].store(n, std::memory_order_relaxed);
     return n;
@@ -979,7 +979,7 @@ hipError_t launch_all(const DecodeArgs& a, hipStream_t stream)
     // a queue in the workspace: the XCDs stream at different rates, and the
     // fixed round-robin spread of a one-chunk-a-workgroup grid leaves the fast
     // ones idle at the end.  Otherwise every chunk is a workgroup of its own.
-    const int resident = resident_blocks(decode_split_kernel<D, PAGED, KV8>, 256);
+    const int resident = resident_blocks<decode_split_kernel<D, PAGED, KV8>>(256);
     if (a.num_splits > 1 && a.queue && resident > 0 && p.items > resident) {
         p.grid = resident;
         p.queue = a.queue;

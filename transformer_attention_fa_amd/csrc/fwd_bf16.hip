@@ -148,6 +148,7 @@ struct Params {
     // at index last_grp), and the divisors gsz * nqb, gsz, glast, H, rep
     int split8, nheads, gsz, glast, last_grp;
     DivConst div_gn, div_gsz, div_glast, div_h, div_rep;
+    int hpb;      // heads per batch in the item list: H, or H / 2 when items pair heads
 };
 
 // Race-hunting build (-DFA_DEBUG_BARRIERS): one more barrier in the middle
@@ -224,7 +225,8 @@ __device__ __forceinline__ int swz(int r, int c)
     else return c ^ ((r >> 1) & 7);
 }
 
-// Order of workgroups: id -> (query block, head, batch).  Workgroups are
+// Order of workgroups: id -> (query block, head, batch); with paired items the
+// "head" is a pair of heads, hpb of them per batch.  Workgroups are
 // dispatched to the 8 XCDs round robin (id % 8).  When the head count divides
 // by 8, XCD x owns the contiguous heads [x*HB/8, (x+1)*HB/8) -- heads that
 // share a KV head land on the same XCD and its L2 -- and walks them in groups
@@ -245,14 +247,19 @@ __device__ __forceinline__ void decompose(int id, const Params& p, bool causal, 
     const int bh = head0 + g0 + rem - j * gcount;
     qb = causal ? p.nqb - 1 - j : j;
     b = div_by(bh, p.div_h);
-    h = bh - b * p.H;
+    h = bh - b * p.hpb;
 }
 
-template <int D, int NW, bool CAUSAL, bool PERSIST, bool STAMPS>
+// PAIR: an item is BM/2 query rows of two heads that share a KV head (head
+// 2i for waves 0-3, head 2i+1 for waves 4-7, the same rows), so both halves
+// read the same K/V tiles and a causal item's diagonal spans two tiles, not four
+template <int D, int NW, bool CAUSAL, bool PERSIST, bool STAMPS, bool PAIR = false>
 __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 {
     static_assert(NW == 8, "the two wave groups pair up on the four SIMDs");
-    constexpr int BM = NW * 32;              // query rows per work item
+    static_assert(!PAIR || (CAUSAL && PERSIST), "paired items are a causal, persistent form");
+    constexpr int BM = NW * 32;              // query rows per work item (all heads)
+    constexpr int BMI = PAIR ? BM / 2 : BM;  // query rows of one head per item
     constexpr int NTHR = NW * 64;
     constexpr int BN = 64;                   // keys per LDS tile
     constexpr int KSTEPS = D / 16;           // MFMA k-steps over d for S^T
@@ -322,23 +329,27 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     };
 
     // ---- work items.  Item (query block, head, batch) covers query rows
-    //      q0 .. q0+BM-1; the per-wave quantities below are set per item.
+    //      q0 .. q0+BMI-1 (of two heads with paired items); the per-wave
+    //      quantities below are set per item.
     struct Item {
-        unsigned bh;     // b * H + h: Q, O and the LSE rows start at bh * N_q
+        unsigned bh;     // b * H + h: Q, O and the LSE rows start at bh * N_q (waves 0-3's head)
+        unsigned bh2;    // waves 4-7's head: bh + 1 with paired items, else bh
         unsigned bg;     // b * H_kv + h / rep: K and V rows start at bg * N_k
         int q0;          // first query row of the block
         int nkb;         // key tiles the block reads: kb_lo .. nkb-1
         int kb_lo;
     };
     auto item_at = [&](int id) __attribute__((always_inline)) {
-        int qb, h, b;
-        decompose(id, p, CAUSAL, qb, h, b);
+        int qb, hh, b;
+        decompose(id, p, CAUSAL, qb, hh, b);
+        const int h = PAIR ? 2 * hh : hh;
         Item it;
         it.bh = (unsigned)(b * p.H + h);
+        it.bh2 = it.bh + (PAIR ? 1u : 0u);
         it.bg = (unsigned)(b * p.H_kv + div_by(h, p.div_rep));
-        it.q0 = qb * BM;
+        it.q0 = qb * BMI;
         int kend = p.N_k;
-        if (CAUSAL) kend = min(p.N_k, it.q0 + BM + off);
+        if (CAUSAL) kend = min(p.N_k, it.q0 + BMI + off);
         it.nkb = kend > 0 ? (kend + BN - 1) / BN : 0;
         it.kb_lo = 0;
         // with a sliding window ("Attention variants" §4: each row sees the W
@@ -354,16 +365,22 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     // Q block of an item into the Q area (16-byte chunks swizzled like a K
     // tile); rows past N_q read as 0.  Q is read once, so the load is
     // non-temporal and leaves L2 to the K/V tiles other items re-read.
+    // Paired items: the Q area's first half holds waves 4-7's head, the second
+    // half waves 0-3's, each the item's BM/2 rows.
     auto issue_q = [&](const Item& it, int part) __attribute__((always_inline)) {
-        const unsigned bytes = (unsigned)max(0, min(BM, p.N_q - it.q0)) * ROWB;
-        const i32x4 rs = make_rsrc(p.q + ((size_t)it.bh * (size_t)p.N_q + (size_t)it.q0) * D, bytes);
+        const bool hi = part >= QPARTS / 2;
+        const unsigned hq = PAIR && !hi ? it.bh2 : it.bh;
+        const int prow = PAIR && hi ? part - QPARTS / 2 : part;    // the part within the head's rows
+        const unsigned bytes = (unsigned)max(0, min(BMI, p.N_q - it.q0)) * ROWB;
+        const i32x4 rs = make_rsrc(p.q + ((size_t)hq * (size_t)p.N_q + (size_t)it.q0) * D, bytes);
         fa_raw_buffer_load_lds(rs, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
-                               ld_voff + part * NTHR * 16, 0, 0, kStreamOnce);
+                               ld_voff + prow * NTHR * 16, 0, 0, kStreamOnce);
     };
 
     Item cur, nxt;
     bool has_next;
     i32x4 rq_nxt;            // the next item's Q block (descriptor), for the steady periods' Q slices
+    i32x4 rq_nxt2;           // paired items: its second half (waves 0-3's head)
     int q_lim;               // steady periods j < q_lim load Q slice j - kb_lo of the next item
     int sb;                  // slot parity: tile t of the current item lives in slot (t + sb) % 2
     int j_knext;             // period that loads the next item's first K tile
@@ -376,7 +393,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     auto set_wave = [&]() __attribute__((always_inline)) {
         kbase = reinterpret_cast<const char*>(p.k + (size_t)cur.bg * (size_t)p.N_k * D);
         vbase = reinterpret_cast<const char*>(p.v + (size_t)cur.bg * (size_t)p.N_k * D);
-        qw0 = cur.q0 + wr * 32;              // first row of this wave
+        qw0 = cur.q0 + (PAIR ? (w & 3) : wr) * 32;   // first row of this wave
         qi = qw0 + l32;                      // this lane's query row
         last_vis = CAUSAL ? min(qi + off, p.N_k - 1) : p.N_k - 1;
         // tiles this wave computes: a_w .. nkb_w-1.  Later tiles lie after its
@@ -690,8 +707,14 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             // one slice a period (items of QPARTS tiles or more), its
             // descriptor made once per item
             const int part = j - q_first;
-            fa_raw_buffer_load_lds(rq_nxt, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
-                                   ld_voff + part * NTHR * 16, 0, 0, kStreamOnce);
+            if constexpr (PAIR) {
+                const bool hi = part >= QPARTS / 2;
+                fa_raw_buffer_load_lds(hi ? rq_nxt2 : rq_nxt, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
+                                       ld_voff + (hi ? part - QPARTS / 2 : part) * NTHR * 16, 0, 0, kStreamOnce);
+            } else {
+                fa_raw_buffer_load_lds(rq_nxt, (LDS_AS void*)(qarea + (part * NTHR + w * 64) * 16), 16,
+                                       ld_voff + part * NTHR * 16, 0, 0, kStreamOnce);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (SM == 1) softmax_phase(j - 1, steadyc);
@@ -954,9 +977,13 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             qpp = 1;
             while (qpp < QPARTS && qpp * qcount < QPARTS) qpp *= 2;
             q_lim = has_next && qpp == 1 ? q_first + QPARTS : q_first;
-            if (has_next)
-                rq_nxt = make_rsrc(p.q + ((size_t)nxt.bh * (size_t)p.N_q + (size_t)nxt.q0) * D,
-                                   (unsigned)max(0, min(BM, p.N_q - nxt.q0)) * ROWB);
+            if (has_next) {
+                const unsigned qbytes = (unsigned)max(0, min(BMI, p.N_q - nxt.q0)) * ROWB;
+                rq_nxt = make_rsrc(p.q + ((size_t)(PAIR ? nxt.bh2 : nxt.bh) * (size_t)p.N_q + (size_t)nxt.q0) * D,
+                                   qbytes);
+                if constexpr (PAIR)
+                    rq_nxt2 = make_rsrc(p.q + ((size_t)nxt.bh * (size_t)p.N_q + (size_t)nxt.q0) * D, qbytes);
+            }
             // this wave's first period (S of tile a_w) ran in the switch period
             // when the wave starts at the item's first tile; its last (PV of
             // tile nkb-1) runs in the next one when it ends at the item's last
@@ -1010,7 +1037,7 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
             has_prev = true;
             do_pv = nkb_w > a_w && nkb_w == cur.nkb;
             j_last = cur.nkb - 1;
-            prev_bh = cur.bh;
+            prev_bh = PAIR && RL == 1 ? cur.bh2 : cur.bh;    // this wave's head
             prev_qw0 = qw0;
             mb = (cur.nkb + sb) & 1;
             has_cur = has_next;
@@ -1036,27 +1063,30 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 // Workgroups that fit on the current device at once: the grid of the
 // persistent kernel.  Cached per device and kernel (host threads may race to
 // fill an entry; they store the same value).
-template <typename K>
-int resident_blocks(K kernel, int threads)
+template <auto Kernel>
+int resident_blocks(int threads)
 {
-    static std::atomic<int> cache[64];
+    static std::atomic<int> cache[64];    // one per instantiation, i.e. per kernel
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
     const int known = cache[dev].load(std::memory_order_relaxed);
     if (known > 0) return known;
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, Kernel, threads, 0) != hipSuccess) return 0;
     const int n = cus * (per_cu > 0 ? per_cu : 1);
     cache[dev].store(n, std::memory_order_relaxed);
     return n;
 }
 
-template <int D, int NW, bool CAUSAL, bool PERSIST, bool STAMPS = false>
+template <int D, int NW, bool CAUSAL, bool PERSIST, bool STAMPS = false, bool PAIR = false>
 hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
 {
     constexpr int BM = NW * 32;
     static_assert(BM == kFwdBf16Rows, "the host checks item counts with this block size");
+    // paired items: half the rows of twice the heads, so no more items than
+    // BM-row blocks of single heads (the host's count bounds both)
+    constexpr int BMI = PAIR ? BM / 2 : BM;
     Params p;
     p.q = static_cast<const uint16_t*>(a.q);
     p.k = static_cast<const uint16_t*>(a.k);
@@ -1069,10 +1099,11 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     p.N_q = a.N_q;
     p.N_k = a.N_k;
     p.rep = a.H / a.H_kv;
-    p.nqb = (a.N_q + BM - 1) / BM;
+    p.hpb = PAIR ? a.H / 2 : a.H;
+    p.nqb = (a.N_q + BMI - 1) / BMI;
     p.group = group < 1 ? 1 : group;
     {
-        const int HB = a.H * a.B;
+        const int HB = p.hpb * a.B;
         p.split8 = (HB & 7) == 0;
         p.nheads = p.split8 ? HB >> 3 : HB;
         p.gsz = p.group < p.nheads ? p.group : p.nheads;
@@ -1081,7 +1112,7 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
         p.div_gn = div_const((unsigned)(p.gsz * p.nqb));
         p.div_gsz = div_const((unsigned)p.gsz);
         p.div_glast = div_const((unsigned)p.glast);
-        p.div_h = div_const((unsigned)a.H);
+        p.div_h = div_const((unsigned)p.hpb);
         p.div_rep = div_const((unsigned)p.rep);
     }
     p.window = CAUSAL ? a.window : 0;
@@ -1089,18 +1120,18 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     // 0 exactly as with scale 0, and masked scores stay -inf instead of NaN
     p.c = a.scale > 0.f ? a.scale * kLog2e : 1e-30f;
     p.stamps = a.clock_stamps;
-    const long long items = (long long)p.nqb * a.H * a.B;   // at most 2^31 - 1: checked on the host
+    const long long items = (long long)p.nqb * p.hpb * a.B;   // at most 2^31 - 1: checked on the host
     if (items == 0) return hipSuccess;
     long long grid = items;
     int xcd = 0;
     if (PERSIST) {
-        const int resident = resident_blocks(fwd_bf16_kernel<D, NW, CAUSAL, PERSIST, STAMPS>, NW * 64);
+        const int resident = resident_blocks<fwd_bf16_kernel<D, NW, CAUSAL, PERSIST, STAMPS, PAIR>>(NW * 64);
         if (resident <= 0) return hipErrorInvalidDevice;
         if (resident < grid) grid = resident;
         if (a.max_workgroups > 0 && a.max_workgroups < grid) grid = a.max_workgroups;
         // the per-XCD split needs whole rows of 8 workgroups (items is then a
         // multiple of 8 too); otherwise the rounds walk the whole list
-        if (((a.H * a.B) & 7) == 0 && grid >= 8) {
+        if (((p.hpb * a.B) & 7) == 0 && grid >= 8) {
             grid = grid / 8 * 8;
             xcd = 1;
         }
@@ -1108,7 +1139,8 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     p.xcd = xcd;
     p.items = (int)items;
     p.grid = (int)grid;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, PERSIST, STAMPS>), dim3((unsigned)grid), dim3(NW * 64), 0, stream, p);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, NW, CAUSAL, PERSIST, STAMPS, PAIR>), dim3((unsigned)grid), dim3(NW * 64), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
@@ -1124,11 +1156,19 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream)
     // d = 128 runs persistent (one workgroup per CU, item switches hidden
     // behind the next item's loads); d = 64 fits two workgroups per CU, which
     // hide each other's start and end, and runs one item per workgroup
-    if (a.d == 128 && a.clock_stamps)   // the test hook's clock record: its own instantiation
+    // Causal items pair two heads that share a KV head when the GQA ratio is
+    // even: the same K/V tiles serve both, and the diagonal, where only the
+    // waves whose rows reach a tile work, spans two tiles instead of four
+    const bool pair = a.causal && (a.H / a.H_kv) % 2 == 0;
+    if (a.d == 128 && a.clock_stamps) {   // the test hook's clock record: its own instantiation
+        if (pair) return launch<128, 8, true, true, true, true>(a, group, stream);
         return a.causal ? launch<128, 8, true, true, true>(a, group, stream)
                         : launch<128, 8, false, true, true>(a, group, stream);
-    if (a.d == 128)
+    }
+    if (a.d == 128) {
+        if (pair) return launch<128, 8, true, true, false, true>(a, group, stream);
         return a.causal ? launch<128, 8, true, true>(a, group, stream) : launch<128, 8, false, true>(a, group, stream);
+    }
     if (a.d == 64)
         return a.causal ? launch<64, 8, true, false>(a, group, stream) : launch<64, 8, false, false>(a, group, stream);
     return hipErrorInvalidValue;
