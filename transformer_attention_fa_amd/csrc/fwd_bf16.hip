@@ -13,6 +13,9 @@
 // gfx950 mapping (not from the pages, whose kernel targets other GPUs):
 //  * work item = (query block of BM = 256 rows, head, batch); workgroup = 8
 //    waves, each wave owns 32 rows of the block; two waves share each SIMD.
+//    Causal launches whose GQA ratio is even pair heads instead: an item is
+//    128 rows of two heads that share a KV head, waves 0-3 on one and 4-7 on
+//    the other, so the causal diagonal spans two K/V tiles instead of four;
 //    At d = 128 the grid is persistent: one workgroup per resident slot
 //    (256 CUs x 1 on MI355X), each working through a list of items; d = 64
 //    fits two workgroups per CU and runs one item per workgroup;
