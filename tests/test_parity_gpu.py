@@ -312,6 +312,31 @@ def test_fwd_random_shapes(case):
     compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
 
 
+# Causal launches with an even GQA ratio at d = 128 pair two heads per item
+# (128 rows each): several blocks per head pair, ragged last blocks, windows
+# that cross blocks, N_q below and above N_k, and capped grids that force
+# several rounds of items per workgroup.
+PAIRED_CASES = [(2, 8, 4, 300, 300, None, 0), (1, 8, 2, 700, 900, None, 3), (2, 4, 1, 513, 513, 100, 5),
+                (1, 6, 3, 1000, 600, None, 2), (3, 4, 2, 129, 2000, 300, 0), (1, 16, 4, 1024, 1024, 200, 8)]
+
+
+@pytest.mark.parametrize("case", PAIRED_CASES, ids=lambda c: "x".join(str(x) for x in c))
+def test_fwd_paired_items(case):
+    import torch
+    B, H, H_kv, N_q, N_k, window, cap = case
+    spec = _spec(B, H, H_kv, N_q, N_k, 128, True, seed=43)
+    say(f"fa_fwd paired items {spec.name} window={window} cap={cap}")
+    data = inputs.prefill_inputs(spec)
+    q, k, v = (bf16_to_device(x) for x in (data.q, data.k, data.v))
+    if cap:
+        o, lse = fwd_capped(q, k, v, True, spec.scale, cap, window)
+    else:
+        o, lse = api.fwd(q, k, v, causal=True, scale=spec.scale, window=window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention(data.q, data.k, data.v, spec.scale, True, window=window)
+    compare(to_f64(o), to_f64(lse), o_ref, lse_ref, BF16_O_TOL, BF16_LSE_REL_TOL, label=spec.name)
+
+
 def _random_f32_cases(n, seed=2027):
     """Seeded fp32 shapes: lengths on and around its 32-key tiles and its
     query blocks, N_q != N_k (both ways), head sharing, both head sizes,
