@@ -65,8 +65,9 @@
 //    takes its next Q fragments from that area, stages its finished 32 x d
 //    output tile in the same rows and stores it as whole rows, then starts
 //    the next item;
-//  * waves 0-3 take the block's later rows: on the causal diagonal those run
-//    longest, and the early-row waves finish before the switch period.
+//  * with single-head items, waves 0-3 take the block's later rows: on the
+//    causal diagonal those run longest, and the early-row waves finish before
+//    the switch period (with paired items both wave groups take the same rows).
 #include "fa_internal.h"
 
 #include <hip/hip_runtime.h>
@@ -287,11 +288,12 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
     const int l32 = lane & 31;
     const int half = lane >> 5;
     const int role = w >> 2;                 // waves w and w+4 share a SIMD
-    // Row groups: waves 0-3 take rows 128-255 of the block, waves 4-7 rows
-    // 0-127.  On the causal diagonal the later rows run longest, and a
-    // matrix-core-first wave ends its last tile with a PV phase alone (its
-    // softmax of that tile ran in the period before), so the item's last
-    // period is short.
+    // Row groups of single-head items: waves 0-3 take rows 128-255 of the
+    // block, waves 4-7 rows 0-127.  On the causal diagonal the later rows run
+    // longest, and a matrix-core-first wave ends its last tile with a PV phase
+    // alone (its softmax of that tile ran in the period before), so the item's
+    // last period is short.  wr is also the wave's 32-row slot in the Q area,
+    // which paired items fill with the second head's rows first.
     const int wr = w ^ 4;
     const int off = p.N_k - p.N_q;           // causal diagonal offset
 
