@@ -51,7 +51,7 @@ def run(B, H, Hkv, Nq, Nk, causal, window, cap, persist=True, group=4, resident=
         HB = hpb * B; head0, nheads, slot = 0, HB, i
         if (HB & 7) == 0:
             nheads = HB >> 3; head0 = (i & 7) * nheads; slot = i >> 3
-        gsz = min(group, nheads)
+        gsz = min(max(1, group // 2) if pair else group, nheads)
         grp = slot // (gsz * nqb); rem = slot - grp * gsz * nqb
         g0 = grp * gsz; gcount = min(gsz, nheads - g0)
         j = rem // gcount; bh = head0 + g0 + rem % gcount

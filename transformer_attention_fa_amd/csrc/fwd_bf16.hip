@@ -1106,7 +1106,10 @@ hipError_t launch(const FwdArgs& a, int group, hipStream_t stream)
     p.rep = a.H / a.H_kv;
     p.hpb = PAIR ? a.H / 2 : a.H;
     p.nqb = (a.N_q + BMI - 1) / BMI;
-    p.group = group < 1 ? 1 : group;
+    // a group of the item order spans `group` heads either way (pairs of heads
+    // with paired items), so that its K/V stays within one XCD's L2
+    p.group = PAIR ? group / 2 : group;
+    if (p.group < 1) p.group = 1;
     {
         const int HB = p.hpb * a.B;
         p.split8 = (HB & 7) == 0;
