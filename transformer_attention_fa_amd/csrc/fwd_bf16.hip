@@ -384,8 +384,9 @@ __global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(Params p)
 
     Item cur, nxt;
     bool has_next;
-    i32x4 rq_nxt;            // the next item's Q block (descriptor), for the steady periods' Q slices
-    i32x4 rq_nxt2;           // paired items: its second half (waves 0-3's head)
+    i32x4 rq_nxt;            // the next item's Q block (descriptor), for the steady periods' Q slices;
+                             // with paired items its first half, waves 4-7's head
+    i32x4 rq_nxt2;           // paired items: its second half, waves 0-3's head
     int q_lim;               // steady periods j < q_lim load Q slice j - kb_lo of the next item
     int sb;                  // slot parity: tile t of the current item lives in slot (t + sb) % 2
     int j_knext;             // period that loads the next item's first K tile
